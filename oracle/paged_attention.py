@@ -94,12 +94,12 @@ def slot_of(table_row, pos: int, B: int) -> int:
 
 
 def slot_mapping(block_tables, seq_idx, positions, B: int) -> np.ndarray:
-    """One slot per (sequence, position) row, int64.  A negative sequence or
-    position, or a table entry of -1, gives -1 (skip)."""
+    """One slot per (sequence, position) row, int64.  A sequence id outside
+    the table, a negative position, or a table entry of -1 gives -1 (skip)."""
     out = np.empty(len(seq_idx), dtype=np.int64)
     for i, (s, p) in enumerate(zip(seq_idx, positions)):
         s, p = int(s), int(p)
-        if s < 0 or p < 0:
+        if s < 0 or s >= block_tables.shape[0] or p < 0:
             out[i] = -1
             continue
         lb = p // B
