@@ -1,0 +1,213 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole hot path for one layer of a decode batch: slot-mapped
+write of each sequence's new K/V row (pa_write_kv), then paged decode
+attention (pa_decode_partials + pa_decode_merge, i.e. pa_decode with 512-token
+partitions).  The default workload is the Llama-3-8B-shaped decode layer:
+64 sequences, 32 query / 8 KV heads, head_dim 128, bf16, B=16, context lengths
+uniform on [512, 4096], pool 1.25x the blocks needed, shuffled.
+
+Inputs are synthetic (seeded) and resident in HBM before timing starts.  To
+keep the 256 MB last-level cache from serving K/V across steps, the step
+rotates over ``--layers`` independent copies of the cache (a model's layers),
+so every step reads its K/V from HBM.
+
+Output: one JSON line (metric, value = GB/s of algorithmic bytes per step
+time, roofline of the dominant kernel from HIP events, CPU-oracle baseline).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "paged decode attention achieved HBM GB/s (% of peak) + tokens/s"
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def make_workload(name):
+    import workloads as W
+    table = {
+        "llama3_8b_decode": W.llama3_8b_decode,
+        "long_context": W.long_context,
+        "shared_prefix_steady": lambda: W.shared_prefix("steady"),
+        "shared_prefix_fork": lambda: W.shared_prefix("fork"),
+        "mixed_lengths_B8": lambda: W.mixed_lengths(8),
+        "mixed_lengths_B16": lambda: W.mixed_lengths(16),
+        "mixed_lengths_B32": lambda: W.mixed_lengths(32),
+    }
+    return table[name]()
+
+
+def algorithmic_bytes(w):
+    """Bytes the decode must move at minimum: K and V of live tokens, q,
+    out, the table entries in use and the context lengths."""
+    e = w.elem_bytes
+    L = w.context_lens.astype(np.int64)
+    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * e
+    q = w.num_seqs * w.num_heads * w.head_dim * e
+    table = int(sum(-(-int(x) // w.block_size) for x in L)) * 4
+    return {"kv": kv, "q": q, "out": q, "table": table, "context_lens": 4 * w.num_seqs,
+            "write": w.num_seqs * w.num_kv_heads * w.head_dim * e * 2 * 2 + 8 * w.num_seqs}
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle (fp64 NumPy, as it is) on this host: one full step
+    (write + decode) of the same workload, repeated until ~budget_s."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    B = w.block_size
+    with threadpool_limits(limits=1):
+        k_pool, v_pool = oracle.new_pools(w.num_blocks, w.num_kv_heads, B, w.head_dim, w.dtype)
+        hs = oracle.slot_mapping(w.hist_block_tables, w.hist_seq, w.hist_pos, B)
+        oracle.write_kv(k_pool, v_pool, oracle.to_bits(w.hist_key, w.dtype),
+                        oracle.to_bits(w.hist_value, w.dtype), hs, B)
+        q = oracle.to_bits(w.q, w.dtype)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            ns = oracle.slot_mapping(w.block_tables, w.new_seq, w.new_pos, B)
+            oracle.write_kv(k_pool, v_pool, oracle.to_bits(w.new_key, w.dtype),
+                            oracle.to_bits(w.new_value, w.dtype), ns, B)
+            oracle.decode(q, k_pool, v_pool, w.block_tables, w.context_lens, w.scale,
+                          w.num_kv_heads, B, w.dtype)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 50:
+                break
+    step_s = el / reps
+    ab = algorithmic_bytes(w)
+    step_bytes = sum(ab.values())
+    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "tokens_per_s": round(w.num_seqs / step_s, 2),
+            "sample": f"{reps} full steps (write + decode, all {w.num_seqs} sequences) of the "
+                      f"same workload, single thread, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_decode")
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    w = make_workload(args.workload)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+
+    import torch
+
+    import paged_kv_cache_307_amd as pa
+    pa.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def t(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    B, P = w.block_size, args.partition
+    hist_bt, bt, cl = t(w.hist_block_tables), t(w.block_tables), t(w.context_lens)
+    k0, v0 = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, B, w.head_dim, dt, dev,
+                               fill=float("nan"))
+    hist_slots = pa.slot_mapping(hist_bt, t(w.hist_seq), t(w.hist_pos), B)
+    pa.write_kv(k0, v0, t(w.hist_key), t(w.hist_value), hist_slots)
+    if len(w.copy_pairs):
+        pa.copy_blocks(k0, v0, t(w.copy_pairs))
+    layers = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(args.layers - 1)]
+    new_slots = pa.slot_mapping(bt, t(w.new_seq), t(w.new_pos), B)
+    new_k, new_v, q = t(w.new_key), t(w.new_value), t(w.q)
+    out = torch.empty_like(q)
+    mcl = w.max_context_len
+    ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, P, dev)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        k, v = layers[i % len(layers)]
+        pa.write_kv(k, v, new_k, new_v, new_slots)
+        if ev is not None:
+            ev[0].record()
+        pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out)
+        if ev is not None:
+            ev[1].record()
+        pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    ab = algorithmic_bytes(w)
+    step_bytes = sum(ab.values())
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    part_avg_ms = float(np.mean(part_ms))
+    part_bytes = ab["kv"] + ab["q"] + ab["table"] + ab["context_lens"]
+    part_gbs = part_bytes / (part_avg_ms * 1e-3) / 1e9
+    L = w.context_lens
+    rec = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.num_seqs, "num_heads": w.num_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": B,
+            "context_len_min": int(L.min()), "context_len_max": int(L.max()),
+            "context_len_mean": round(float(L.mean()), 1), "num_blocks": w.num_blocks,
+            "partition_size": P, "layers_rotated": args.layers,
+            "step": "pa_write_kv + pa_decode_partials + pa_decode_merge",
+        },
+        "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": {
+            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B}> (pa_decode_partials)",
+            "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
+            "avg_us": round(part_avg_ms * 1e3, 3), "bytes_per_launch": part_bytes,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

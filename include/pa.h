@@ -1,0 +1,227 @@
+/*
+ * pa.h -- C ABI of the paged KV-cache decode library (libpa.so, gfx950).
+ *
+ * The hot path of PagedAttention: each sequence's K/V live in fixed-size
+ * physical blocks of B tokens that need not be adjacent; a per-sequence block
+ * table maps logical block i to a physical block id, so logical token t sits
+ * in block block_table[t / B] at offset t % B.  Pages this follows:
+ *
+ *   [P1] "什么是 PagedAttention？" (qubittool glossary): 映射逻辑块与物理块
+ *        (logical -> physical block mapping), 共享但不污染状态 (sharing and
+ *        copy-on-write of a shared partial block).
+ *   [P2] "PagedAttention学习笔记" (juejin): section 2.1 (ceil(L/B) blocks,
+ *        block i holds tokens [iB, min((i+1)B, L))), section 三 (the kernel
+ *        reads Q and the block table, gathers K/V by block, computes
+ *        softmax(QK^T)V), and the BlockTable walkthrough (int32 table of
+ *        [max_num_reqs, max_num_blocks_per_req]; slot = block_id * B +
+ *        pos % B; -1 marks an entry this rank does not own).
+ *   [P3] "KV cache 显存管理：为什么 PagedAttention 是 vLLM 的核心" (mini-vLLM
+ *        blog): PagedAttention 改变了什么 (logical_block = t // B, offset =
+ *        t % B, physical = block_table[logical]) and 对 ModelRunner 的影响
+ *        (the kernel is given the current token, each sequence's context
+ *        length and block table, the physical block pool, and the slot of the
+ *        current token's K/V).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every pointer argument is a device pointer to memory the caller
+ *           owns (hipMalloc'ed or a torch tensor's storage).  The library
+ *           allocates nothing and keeps no state; calls are thread-safe.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *           stream).  Every call only enqueues work on it and returns; results
+ *           are visible after the stream is synchronised.  Device-side faults
+ *           surface at that synchronisation.
+ * Errors.   Every argument is checked on the host before anything is
+ *           launched; a failing check returns a negative PA_ERR_* and enqueues
+ *           nothing.  A call whose work is empty (zero tokens, sequences or
+ *           pairs) returns PA_OK without launching.  A failed launch returns
+ *           PA_ERR_HIP.  pa_status_string() names a status.
+ * Element types.
+ *           PA_DTYPE_F32 (IEEE binary32) or PA_DTYPE_BF16 (bfloat16).  q, the
+ *           K/V pools, key/value and out of one call share the dtype.
+ *           Accumulation is always fp32; outputs are rounded to the dtype with
+ *           round-to-nearest-even.
+ * Cache layout (both pools, row-major, element offsets):
+ *           k_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *           v_cache [num_blocks][num_kv_heads][head_dim][block_size]
+ *           Slot s names block s / block_size, offset s % block_size in both.
+ *           The pages leave the layout to the implementation; this one makes
+ *           each (block, KV head) tile of K and of V one contiguous run of
+ *           block_size * head_dim elements, with V's tokens innermost so the
+ *           P.V contraction reads them directly as matrix-core operands.
+ * Supported shapes.
+ *           head_dim in {64, 128, 256}; block_size in {8, 16, 32};
+ *           num_heads % num_kv_heads == 0 and num_heads / num_kv_heads <= 16.
+ * Grouped-query attention.
+ *           Query head h reads KV head h / (num_heads / num_kv_heads).
+ * Memory safety.
+ *           Kernels never access memory outside the documented extents even
+ *           when a precondition is broken: an out-of-range block id or slot
+ *           is skipped by writes and copies, and makes the affected decode
+ *           outputs NaN.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent sizes      */
+  PA_ERR_UNSUPPORTED = -2, /* a head_dim / block_size / dtype / group size not built */
+  PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required            */
+  PA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed            */
+};
+
+enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pa_status_string(int status);
+
+/*
+ * pa_slot_mapping -- flat cache slot of each (sequence, position) row.
+ * [P2 BlockTable walkthrough: block_id = block_table[req, pos // B],
+ *  slot = block_id * B + pos % B; -1 = not written by this rank.]
+ *
+ *   slot_mapping  out  int64 [num_tokens]
+ *   block_tables  in   int32 [num_seqs][max_blocks_per_seq]
+ *   seq_ids       in   int32 [num_tokens]  sequence of each row
+ *   positions     in   int32 [num_tokens]  logical token position of each row
+ *
+ * A row gets -1 when its sequence id is outside [0, num_seqs), when its
+ * position is negative, when the position's logical block is >=
+ * max_blocks_per_seq, or when the table entry there is negative.  Returns PA_ERR_INVALID_ARG for null pointers (with
+ * num_tokens > 0), negative sizes, or block_size < 1.
+ */
+int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables, const int32_t* seq_ids,
+                    const int32_t* positions, int32_t num_tokens, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t block_size, void* stream);
+
+/*
+ * pa_write_kv -- store each token's K and V rows at its slot.
+ * [P3 对 ModelRunner 的影响: the slot is where the current token's K/V go;
+ *  P2 section 三: slot -1 is skipped.]
+ *
+ *   k_cache, v_cache  in/out  pools in the layout above, num_blocks blocks
+ *   key, value        in      [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping      in      int64 [num_tokens]
+ *
+ * Row i is written to block slot_mapping[i] / block_size, offset
+ * slot_mapping[i] % block_size.  Rows with a negative slot, or a slot
+ * >= num_blocks * block_size, are skipped.  Non-negative slots must be
+ * distinct within one call (two rows for one slot leave either row there).
+ * The result is bit-exact: the stored bits are the input bits.
+ */
+int pa_write_kv(void* k_cache, void* v_cache, const void* key, const void* value,
+                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                void* stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write of whole blocks.
+ * [P1 共享但不污染状态: a sequence about to write into a shared partial block
+ *  gets a private block holding a copy of the valid entries; only that
+ *  sequence's table changes, the original keeps its other references.]
+ *
+ *   k_cache, v_cache  in/out  pools in the layout above
+ *   block_mapping     in      int64 [num_pairs][2] = (src, dst)
+ *
+ * For each pair, K block dst and V block dst (all KV heads, all slots)
+ * become bit-exact copies of block src.  Pairs with an id outside
+ * [0, num_blocks) are skipped.  The dst ids must be distinct and disjoint
+ * from the src ids of the same call.  Updating block tables is the
+ * caller's part (host-side block management).
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t dtype, void* stream);
+
+/*
+ * Split-KV workspace.  A context of length L is split into partitions of
+ * partition_size tokens, partition p holding tokens
+ * [p * partition_size, min((p + 1) * partition_size, L)).  Each partition
+ * yields one record per (sequence, KV head) of
+ *   float o[G][head_dim], m[G], l[G]      (G = num_heads / num_kv_heads)
+ * padded to R = G * head_dim + 4 * ceil(G / 2) floats, where, over the
+ * partition's tokens t and with x_t = scale * log2(e) * q.k_t,
+ *   m = max_t x_t,  l = sum_t 2^(x_t - m),  o = sum_t 2^(x_t - m) v_t.
+ * Record (s, g, p) starts at float offset
+ *   ((s * num_kv_heads + g) * max_partitions + p) * R,
+ * max_partitions = ceil(max_context_len / partition_size).  The workspace
+ * must be 16-byte aligned.
+ * pa_decode_workspace_bytes returns the byte size of that array (0 when
+ * partition_size == 0, i.e. single pass, or when there is nothing to do).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/*
+ * pa_decode -- one decode step of attention over the paged cache.
+ * [P2 section 三 and section 2.1; P3 PagedAttention 改变了什么: the attention
+ *  formula is unchanged, only the K/V access path goes through the table.]
+ *
+ *   out           out [num_seqs][num_heads][head_dim]
+ *   q             in  [num_seqs][num_heads][head_dim]
+ *   k_cache, v_cache  in  pools in the layout above
+ *   block_tables  in  int32 [num_seqs][max_blocks_per_seq], -1 padded
+ *   context_lens  in  int32 [num_seqs]: tokens attended by sequence s,
+ *                     including the one written this step (position L - 1)
+ *   max_context_len   host-side upper bound of context_lens (sizes the grid)
+ *   scale             multiplies q.k before the softmax (typically 1/sqrt(D))
+ *   partition_size    0: single pass, no workspace needed.  Otherwise split
+ *                     the context into partitions of this many tokens (a
+ *                     multiple of 16 and of block_size) and merge them with a
+ *                     log-sum-exp reduction.
+ *   workspace, workspace_bytes  >= pa_decode_workspace_bytes(...) when
+ *                     partition_size > 0; may be NULL/0 otherwise.
+ *
+ * out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t over t < L_s, with
+ * K_t, V_t read from block block_tables[s][t / B] at offset t % B and KV head
+ * h / G.  A sequence with L_s == 0 gets zeros; context_lens[s] larger than
+ * max_context_len or max_blocks_per_seq * block_size is clamped to the
+ * smaller.  Table entries at or past ceil(L_s / B) are never read.  Slots of
+ * the last block past L_s are never used (they may hold anything, NaN
+ * included).  Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED /
+ * PA_ERR_WORKSPACE on a failed check.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+              void* stream);
+
+/*
+ * pa_decode_partials / pa_decode_merge -- the two phases pa_decode runs when
+ * partition_size > 0, callable one by one (same arguments as pa_decode).
+ * pa_decode_partials writes the record of every (s, g, p) with p <
+ * ceil(L_s / partition_size) when that count is >= 2; sequences with a single
+ * partition (or L_s == 0) get their final output written to out directly and
+ * no record.  pa_decode_merge combines the records of each sequence with two
+ * or more partitions, M = max_p m_p, w_p = 2^(m_p - M),
+ * out = sum_p w_p o_p / sum_p w_p l_p, and leaves the other rows of out
+ * untouched.
+ */
+int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_context_len, float scale, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                    const void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,26 @@
+"""MI355X-native paged KV-cache decode path (PagedAttention hot path).
+
+The product is ``libpa.so`` (HIP kernels for gfx950 behind the C ABI of
+``include/pa.h``); this package is its thin Python binding plus the build
+script.  PyTorch provides device memory and streams only.
+"""
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    PA_DTYPE_BF16,
+    PA_DTYPE_F32,
+    PagedAttentionError,
+    alloc_workspace,
+    copy_blocks,
+    decode,
+    decode_merge,
+    decode_partials,
+    decode_workspace_bytes,
+    empty_kv_cache,
+    kv_cache_shapes,
+    library_path,
+    load_library,
+    slot_mapping,
+    status_string,
+    write_kv,
+)

@@ -1,0 +1,281 @@
+// C ABI of libpa: host-side argument checks, launch geometry, dispatch.
+// Every check runs before anything is enqueued; see include/pa.h for the
+// contract of each entry point.
+
+#include <math.h>
+
+#include "internal.h"
+#include "pa.h"
+
+namespace {
+
+using pa::DecodeArgs;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes_of(int32_t dtype) {
+  switch (dtype) {
+    case PA_DTYPE_F32: return 4;
+    case PA_DTYPE_BF16: return 2;
+    default: return 0;
+  }
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool supported_block_size(int32_t b) { return b == 8 || b == 16 || b == 32; }
+
+// Shape checks common to pa_write_kv / pa_copy_blocks.
+int check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, int32_t dtype) {
+  const int eb = elem_bytes_of(dtype);
+  if (eb == 0) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 0)
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t(head_dim) * eb) % 16 != 0) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+struct DecodePlan {
+  DecodeArgs args;
+  int head_dim;
+  int block_size;
+  bool bf16;
+  bool split;  // records + merge needed
+};
+
+int64_t effective_max_len(int32_t max_context_len, int32_t max_blocks_per_seq, int32_t block_size) {
+  const int64_t cap = int64_t(max_blocks_per_seq) * block_size;
+  return max_context_len < cap ? max_context_len : cap;
+}
+
+int64_t workspace_bytes_for(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim,
+                            int64_t max_partitions) {
+  return int64_t(num_seqs) * num_kv_heads * max_partitions * pa::record_floats(group, head_dim) *
+         int64_t(sizeof(float));
+}
+
+// Validate the decode arguments and fill the launch plan.  Returns PA_OK with
+// plan->args.num_seqs == 0 when there is nothing to do.
+int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                size_t workspace_bytes, int32_t dtype) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_blocks < 0 ||
+      max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (elem_bytes_of(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  const int32_t group = num_heads / num_kv_heads;
+  if (group > 16) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  plan->args = DecodeArgs{};
+  plan->args.num_seqs = 0;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARG;
+
+  const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
+  const int unit = block_size > 16 ? block_size : 16;
+  int64_t part = partition_size;
+  int64_t max_parts = 1;
+  if (part > 0) {
+    max_parts = max_len > 0 ? (max_len + part - 1) / part : 1;
+  } else {
+    part = max_len > 0 ? ((max_len + unit - 1) / unit) * unit : unit;
+  }
+  if (max_parts <= 1) {
+    max_parts = 1;
+    part = max_len > 0 ? ((max_len + unit - 1) / unit) * unit : unit;
+  }
+  const int64_t grid = int64_t(num_seqs) * num_kv_heads * max_parts;
+  if (grid > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  plan->split = max_parts > 1;
+  if (plan->split) {
+    const int64_t need = workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, max_parts);
+    if (!workspace || int64_t(workspace_bytes) < need || !aligned16(workspace))
+      return PA_ERR_WORKSPACE;
+  }
+
+  DecodeArgs& a = plan->args;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.ws = plan->split ? static_cast<float*>(workspace) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = int32_t(max_len);
+  a.partition_size = int32_t(part);
+  a.max_partitions = int32_t(max_parts);
+  a.scale_log2e = scale * 1.4426950408889634f;
+  plan->head_dim = head_dim;
+  plan->block_size = block_size;
+  plan->bf16 = dtype == PA_DTYPE_BF16;
+  return PA_OK;
+}
+
+hipError_t launch_partials(const DecodePlan& plan, hipStream_t stream) {
+  if (plan.bf16) return pa::launch_decode_bf16_mfma(plan.args, plan.head_dim, plan.block_size, stream);
+  return pa::launch_decode_simt(plan.args, plan.head_dim, plan.block_size, false, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG: invalid argument";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables, const int32_t* seq_ids,
+                    const int32_t* positions, int32_t num_tokens, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, int32_t block_size, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || block_size < 1)
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !seq_ids || !positions) return PA_ERR_INVALID_ARG;
+  if (!block_tables && int64_t(num_seqs) * max_blocks_per_seq > 0) return PA_ERR_INVALID_ARG;
+  return status_of(pa::launch_slot_mapping(slot_mapping, block_tables, seq_ids, positions,
+                                           num_tokens, num_seqs, max_blocks_per_seq, block_size,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int pa_write_kv(void* k_cache, void* v_cache, const void* key, const void* value,
+                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                void* stream) {
+  if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+  const int st = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_cache || !v_cache || !key || !value || !slot_mapping) return PA_ERR_INVALID_ARG;
+  const int eb = elem_bytes_of(dtype);
+  if (!aligned16(k_cache) || !aligned16(key) ||
+      (reinterpret_cast<uintptr_t>(v_cache) % eb) || (reinterpret_cast<uintptr_t>(value) % eb))
+    return PA_ERR_INVALID_ARG;
+  return status_of(pa::launch_write_kv(k_cache, v_cache, key, value, slot_mapping, num_tokens,
+                                       num_kv_heads, head_dim, block_size, num_blocks, eb,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                   int32_t dtype, void* stream) {
+  if (num_pairs < 0) return PA_ERR_INVALID_ARG;
+  const int st = check_cache_shape(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !block_mapping) return PA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_INVALID_ARG;
+  if (int64_t(num_pairs) * 2 > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  return status_of(pa::launch_copy_blocks(k_cache, v_cache, block_mapping, num_pairs, num_kv_heads,
+                                          head_dim, block_size, num_blocks, elem_bytes_of(dtype),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len <= 0 || partition_size <= 0 || num_heads % num_kv_heads != 0)
+    return 0;
+  const int64_t parts = (int64_t(max_context_len) + partition_size - 1) / partition_size;
+  if (parts <= 1) return 0;
+  return size_t(workspace_bytes_for(num_seqs, num_kv_heads, num_heads / num_kv_heads, head_dim, parts));
+}
+
+int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_context_len, float scale, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+  DecodePlan plan;
+  const int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                             workspace_bytes, dtype);
+  if (st != PA_OK || plan.args.num_seqs == 0) return st;
+  return status_of(launch_partials(plan, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                    int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                    const void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 0 ||
+      max_context_len < 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
+    return PA_ERR_INVALID_ARG;
+  if (elem_bytes_of(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || partition_size == 0) return PA_OK;
+  const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
+  const int64_t parts = max_len > 0 ? (max_len + partition_size - 1) / partition_size : 1;
+  if (parts <= 1) return PA_OK;
+  if (!out || !context_lens) return PA_ERR_INVALID_ARG;
+  const int32_t group = num_heads / num_kv_heads;
+  if (!workspace || !aligned16(workspace) ||
+      int64_t(workspace_bytes) < workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts))
+    return PA_ERR_WORKSPACE;
+  if (int64_t(num_seqs) * num_kv_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  DecodeArgs a{};
+  a.out = out;
+  a.context_lens = context_lens;
+  a.ws = static_cast<float*>(const_cast<void*>(workspace));
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = int32_t(max_len);
+  a.partition_size = partition_size;
+  a.max_partitions = int32_t(parts);
+  return status_of(pa::launch_decode_merge(a, head_dim, block_size, dtype == PA_DTYPE_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+              int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+              int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+              void* stream) {
+  DecodePlan plan;
+  const int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                             workspace_bytes, dtype);
+  if (st != PA_OK || plan.args.num_seqs == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_partials(plan, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (plan.split) e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);
+  return status_of(e);
+}
+
+}  // extern "C"

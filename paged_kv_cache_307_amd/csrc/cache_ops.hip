@@ -1,0 +1,122 @@
+// Slot mapping, KV write and copy-on-write block copy kernels.
+//
+// [P2 "PagedAttention学习笔记", BlockTable walkthrough] slot = block_id * B +
+// pos % B with block_id = block_table[req, pos // B]; -1 = not this rank's row.
+// [P3 "KV cache 显存管理", 对 ModelRunner 的影响] the current token's K/V are
+// written at its slot.  [P1 "什么是 PagedAttention？", 共享但不污染状态] a
+// writer to a shared partial block first gets a private copy.
+//
+// All three are HBM-bound byte movers; each 64-lane wave moves whole 16-byte
+// vectors where the layout is contiguous (K rows, whole blocks) and single
+// elements where it is strided (V's token-innermost rows).
+
+#include "device_common.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void slot_mapping_kernel(
+    int64_t* __restrict__ slots, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions, int num_tokens,
+    int num_seqs, int max_blocks_per_seq, int block_size) {
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= num_tokens) return;
+  const int s = seq_ids[i];
+  const int pos = positions[i];
+  int64_t slot = -1;
+  if (s >= 0 && s < num_seqs && pos >= 0) {
+    const int logical = pos / block_size;
+    if (logical < max_blocks_per_seq) {
+      const int32_t block = block_tables[int64_t(s) * max_blocks_per_seq + logical];
+      if (block >= 0) slot = int64_t(block) * block_size + pos % block_size;
+    }
+  }
+  slots[i] = slot;
+}
+
+// One workgroup per token row.  K rows are contiguous (head_dim elements per
+// KV head) and move as 16-byte vectors; V stores each element at stride
+// block_size (tokens innermost).
+template <typename Elem>
+__global__ __launch_bounds__(kThreads) void write_kv_kernel(
+    Elem* __restrict__ k_cache, Elem* __restrict__ v_cache, const Elem* __restrict__ key,
+    const Elem* __restrict__ value, const int64_t* __restrict__ slots, int num_kv_heads,
+    int head_dim, int block_size, int num_blocks) {
+  const int i = blockIdx.x;
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= int64_t(num_blocks) * block_size) return;
+  const int64_t block = slot / block_size;
+  const int off = int(slot % block_size);
+  const int row = num_kv_heads * head_dim;            // elements per token row
+  const int64_t block_elems = int64_t(row) * block_size;
+
+  constexpr int kVec = 16 / sizeof(Elem);
+  const int row_vecs = row / kVec;
+  const int dim_vecs = head_dim / kVec;
+  const uint4* src_k = reinterpret_cast<const uint4*>(key + int64_t(i) * row);
+  for (int v = threadIdx.x; v < row_vecs; v += kThreads) {
+    const int h = v / dim_vecs;
+    const int dv = v % dim_vecs;
+    Elem* dst = k_cache + block * block_elems + (int64_t(h) * block_size + off) * head_dim;
+    reinterpret_cast<uint4*>(dst)[dv] = src_k[v];
+  }
+  const Elem* src_v = value + int64_t(i) * row;
+  Elem* vblk = v_cache + block * block_elems + off;
+  for (int e = threadIdx.x; e < row; e += kThreads) {
+    // e = h * head_dim + d  ->  v_cache[block][h][d][off]
+    vblk[int64_t(e) * block_size] = src_v[e];
+  }
+}
+
+// One workgroup per (pair, pool): copies a whole block of one pool.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const int64_t* __restrict__ pairs,
+    int64_t block_vecs, int num_blocks) {
+  const int pair = blockIdx.x >> 1;
+  uint4* pool = (blockIdx.x & 1) ? v_cache : k_cache;
+  const int64_t src = pairs[2 * int64_t(pair)];
+  const int64_t dst = pairs[2 * int64_t(pair) + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const uint4* from = pool + src * block_vecs;
+  uint4* to = pool + dst * block_vecs;
+  for (int64_t v = threadIdx.x; v < block_vecs; v += kThreads) to[v] = from[v];
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_tables, const int32_t* seq_ids,
+                               const int32_t* positions, int num_tokens, int num_seqs,
+                               int max_blocks_per_seq, int block_size, hipStream_t stream) {
+  return launch(slot_mapping_kernel, dim3(ceil_div(num_tokens, kThreads)), dim3(kThreads), 0,
+                stream, slots, block_tables, seq_ids, positions, num_tokens, num_seqs,
+                max_blocks_per_seq, block_size);
+}
+
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const void* value,
+                           const int64_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int elem_bytes, hipStream_t stream) {
+  if (elem_bytes == 4) {
+    return launch(write_kv_kernel<uint32_t>, dim3(num_tokens), dim3(kThreads), 0, stream,
+                  static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                  static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value), slots,
+                  num_kv_heads, head_dim, block_size, num_blocks);
+  }
+  return launch(write_kv_kernel<uint16_t>, dim3(num_tokens), dim3(kThreads), 0, stream,
+                static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), slots,
+                num_kv_heads, head_dim, block_size, num_blocks);
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              int elem_bytes, hipStream_t stream) {
+  const int64_t block_vecs = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes / 16;
+  return launch(copy_blocks_kernel, dim3(2 * num_pairs), dim3(kThreads), 0, stream,
+                static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pairs, block_vecs,
+                num_blocks);
+}
+
+}  // namespace pa

@@ -1,0 +1,78 @@
+// Internal declarations shared by the HIP sources of libpa (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <tuple>
+#include <utility>
+
+namespace pa {
+
+// Arguments of one decode launch (partials or single pass) and of the merge.
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws;                  // split-KV records, nullptr when max_partitions == 1
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;              // num_heads / num_kv_heads
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;    // clamp for context_lens
+  int32_t partition_size;     // tokens per partition (multiple of 16 and of B)
+  int32_t max_partitions;     // ceil(max_context_len / partition_size), >= 1
+  float scale_log2e;          // scale * log2(e)
+};
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Floats in one split-KV record: o[G][D], then m[G], l[G], padded so every
+// record starts on a 16-byte boundary.
+__host__ __device__ inline int64_t record_floats(int group, int head_dim) {
+  return int64_t(group) * head_dim + 4 * ((group + 1) / 2);
+}
+
+// Launch `kernel` and return hipLaunchKernel's own status (never a stale
+// error left by an earlier call).  Arguments are converted to the kernel's
+// parameter types first.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shmem,
+                  hipStream_t stream, Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count mismatch");
+  std::tuple<KArgs...> values(std::forward<Args>(args)...);
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&](auto&... v) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&v)), ...);
+  }, values);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, shmem, stream);
+}
+
+// Launchers (each returns hipSuccess or the launch error).
+hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_tables, const int32_t* seq_ids,
+                               const int32_t* positions, int num_tokens, int num_seqs,
+                               int max_blocks_per_seq, int block_size, hipStream_t stream);
+hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const void* value,
+                           const int64_t* slots, int num_tokens, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int elem_bytes, hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
+                              int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                              int elem_bytes, hipStream_t stream);
+
+// Decode partials / single pass.  Returns hipErrorInvalidValue for a shape
+// with no compiled kernel (the API checks shapes first).
+hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_size,
+                                   hipStream_t stream);
+hipError_t launch_decode_simt(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
+                              hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
+                               hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,90 @@
+"""Helpers for the GPU parity tests: move a workload to the device and run one
+decode step through the C ABI (slot mapping -> history write -> copy-on-write
+-> step write -> decode), and compare with the oracle."""
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_307_amd as pa
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def torch_dtype(w):
+    return torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+
+def dev(x, w=None, device="cuda"):
+    """numpy -> device tensor; element storage (uint16 bf16 bits) -> bf16."""
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(x).to(device)
+
+
+def bits(t):
+    """Device tensor -> numpy raw bits (uint16 for bf16, uint32 for f32)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32).numpy().view(np.uint32)
+    return t.numpy()
+
+
+def as_f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def pools_from_oracle(w, k_bits, v_bits):
+    return dev(k_bits if w.dtype == "bf16" else k_bits.view(np.float32)), \
+        dev(v_bits if w.dtype == "bf16" else v_bits.view(np.float32))
+
+
+def run_step(w, partition_size=0, device="cuda", keep=False):
+    """The product path on one workload; returns a dict of device tensors."""
+    dt = torch_dtype(w)
+    k, v = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, dt,
+                             device, fill=float("nan"))
+    hist_bt = dev(w.hist_block_tables)
+    hist_slots = pa.slot_mapping(hist_bt, dev(w.hist_seq), dev(w.hist_pos), w.block_size)
+    pa.write_kv(k, v, dev(w.hist_key), dev(w.hist_value), hist_slots)
+    if len(w.copy_pairs):
+        pa.copy_blocks(k, v, dev(w.copy_pairs))
+    bt = dev(w.block_tables)
+    new_slots = pa.slot_mapping(bt, dev(w.new_seq), dev(w.new_pos), w.block_size)
+    pa.write_kv(k, v, dev(w.new_key), dev(w.new_value), new_slots)
+    cl = dev(w.context_lens)
+    out = pa.decode(dev(w.q), k, v, bt, cl, w.max_context_len, w.scale,
+                    partition_size=partition_size)
+    torch.cuda.synchronize()
+    r = {"out": out, "hist_slots": hist_slots, "new_slots": new_slots, "bt": bt, "cl": cl}
+    if keep:
+        r["k"], r["v"] = k, v
+    return r
+
+
+def max_err(gpu_out, ref, seqs=None, kv_heads=None, w=None):
+    got = as_f64(gpu_out)
+    if seqs is not None:
+        G = w.num_heads // w.num_kv_heads
+        rows = [(s, h) for s in seqs for g in kv_heads for h in range(g * G, (g + 1) * G)]
+        idx = tuple(np.array(rows).T)
+        return float(np.max(np.abs(got[idx] - ref[idx])))
+    assert not np.isnan(ref).any()
+    return float(np.max(np.abs(got - ref)))
+
+
+def assert_pool_equal(w, k_dev, v_dev, k_ref_bits, v_ref_bits):
+    """Bit-exact pool comparison, done on the device for big pools."""
+    kd = k_dev.view(torch.int16 if w.dtype == "bf16" else torch.int32)
+    vd = v_dev.view(torch.int16 if w.dtype == "bf16" else torch.int32)
+    kr = torch.from_numpy(k_ref_bits.view(np.int16 if w.dtype == "bf16" else np.int32)).to(kd.device)
+    vr = torch.from_numpy(v_ref_bits.view(np.int16 if w.dtype == "bf16" else np.int32)).to(vd.device)
+    assert torch.equal(kd, kr), "K pool differs from the oracle's"
+    assert torch.equal(vd, vr), "V pool differs from the oracle's"
+
+
+def oracle_out(w, seqs=None, kv_heads=None):
+    return oracle.run_step(w, seqs=seqs, kv_heads=kv_heads)

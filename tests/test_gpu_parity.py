@@ -1,0 +1,200 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+Bit-exact: slot mappings, pools after writes and copies.  Within tolerance
+(max abs, fp32 1e-5, bf16 2e-2 with fp32 accumulation): decode outputs, at
+small sizes element by element and at the five full workload sizes on every
+or on sampled (sequence, KV head) units.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_307_amd as pa
+import workloads as W
+from gpu_common import TOL, as_f64, assert_pool_equal, bits, dev, max_err, pools_from_oracle, run_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _check_step(w, partition_size, seqs=None, kv_heads=None, check_pool=True):
+    _say(f"{w.name} S={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
+         f"B={w.block_size} {w.dtype} P={partition_size}")
+    ref = oracle.run_step(w, seqs=seqs, kv_heads=kv_heads)
+    r = run_step(w, partition_size, keep=True)
+    assert np.array_equal(bits(r["hist_slots"]), ref["hist_slots"])
+    assert np.array_equal(bits(r["new_slots"]), ref["new_slots"])
+    if check_pool:
+        assert_pool_equal(w, r["k"], r["v"], ref["k_pool"], ref["v_pool"])
+    err = max_err(r["out"], ref["out"], seqs, kv_heads, w)
+    print(f"[case] max abs err {err:.3e} (tol {TOL[w.dtype]})", flush=True)
+    assert err <= TOL[w.dtype]
+    return r, ref
+
+
+# ------------------------------------------------------------- small, exhaustive
+
+@pytest.mark.parametrize("P", [0, 16, 32, 64])
+def test_tiny_f32(P):
+    _check_step(W.tiny_f32(), P)
+
+
+@pytest.mark.parametrize("P", [0, 16, 48])
+def test_tiny_shape_bf16(P):
+    w = W.custom([1, 17, 40, 100], 4, 2, 64, 16, "bf16", seed=307_011, name="tiny_bf16")
+    _check_step(w, P)
+
+
+RAGGED = list(range(1, 41)) + [63, 64, 65, 127, 128, 129, 255, 257, 511, 512, 513, 700]
+
+SHAPES = [  # (Hq, Hkv, D, B, dtype)
+    (4, 2, 64, 16, "bf16"), (32, 8, 128, 16, "bf16"), (64, 8, 128, 8, "bf16"),
+    (64, 8, 128, 32, "bf16"), (16, 1, 128, 16, "bf16"), (8, 8, 64, 16, "bf16"),
+    (32, 2, 256, 16, "bf16"), (12, 4, 128, 8, "bf16"),
+    (4, 2, 64, 16, "f32"), (32, 8, 128, 8, "f32"), (16, 16, 256, 32, "f32"), (6, 2, 64, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "Hq%d_Hkv%d_D%d_B%d_%s" % s)
+def test_ragged_lengths(shape):
+    Hq, Hkv, D, B, dt = shape
+    w = W.custom(RAGGED, Hq, Hkv, D, B, dt, seed=307_020 + Hq + D + B)
+    for P in (0, max(32, B), 512):
+        _check_step(w, P)
+
+
+def test_split_phases_equal_decode():
+    w = W.custom([5, 100, 600, 1500], 32, 8, 128, 16, "bf16", seed=307_031)
+    r = run_step(w, 0, keep=True)
+    ws = pa.alloc_workspace(w.num_seqs, 32, 8, 128, w.max_context_len, 64)
+    q = dev(w.q)
+    full = pa.decode(q, r["k"], r["v"], r["bt"], r["cl"], w.max_context_len, w.scale,
+                     partition_size=64, workspace=ws)
+    out = torch.empty_like(q)
+    pa.decode_partials(q, r["k"], r["v"], r["bt"], r["cl"], w.max_context_len, w.scale, 64, ws, out)
+    pa.decode_merge(out, r["cl"], 8, 16, w.max_blocks_per_seq, w.max_context_len, 64, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, full)
+    ref = oracle.run_step(w)["out"]
+    assert np.max(np.abs(as_f64(out) - ref)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_zero_and_short_lengths_decode(dt):
+    """Decode only, on the oracle's pool, with some context lengths cut to 0
+    and others shortened: L = 0 gives zeros, the rest match the oracle."""
+    w = W.custom([30, 70, 1, 200, 16], 8, 2, 64, 16, dt, seed=307_041)
+    ref = oracle.run_step(w)
+    lens = np.array([0, 33, 0, 129, 16], np.int32)
+    want = oracle.decode(oracle.to_bits(w.q, dt), ref["k_pool"], ref["v_pool"], w.block_tables,
+                         lens, w.scale, w.num_kv_heads, w.block_size, dt)
+    k, v = pools_from_oracle(w, ref["k_pool"], ref["v_pool"])
+    for P in (0, 16, 64):
+        _say(f"zero/short lengths {dt} P={P}")
+        out = pa.decode(dev(w.q), k, v, dev(w.block_tables), dev(lens), int(lens.max()), w.scale,
+                        partition_size=P)
+        torch.cuda.synchronize()
+        got = as_f64(out)
+        assert np.all(got[[0, 2]] == 0.0)
+        assert np.max(np.abs(got - want)) <= TOL[dt]
+
+
+def test_single_token_is_exact_copy():
+    """L = 1: the output is the token's V row, bit for bit after rounding."""
+    w = W.custom([1, 1, 1], 8, 4, 128, 16, "bf16", seed=307_051)
+    r = run_step(w, 0)
+    G = 2
+    want = np.repeat(w.new_value, G, axis=1)  # [S, Hq, D] bf16 bits
+    assert np.array_equal(bits(r["out"]), want)
+
+
+# ------------------------------------------------------------- write / copy / slots
+
+def test_write_skips_negative_and_out_of_range_slots():
+    w = W.custom([40, 17], 4, 2, 64, 16, "bf16", seed=307_061)
+    ref = oracle.run_step(w)
+    k, v = pools_from_oracle(w, ref["k_pool"], ref["v_pool"])
+    k0, v0 = bits(k), bits(v)
+    cap = w.num_blocks * w.block_size
+    slots = torch.tensor([-1, cap, cap + 7, -5], dtype=torch.int64, device="cuda")
+    rows = torch.zeros((4, 2, 64), dtype=torch.bfloat16, device="cuda")
+    pa.write_kv(k, v, rows, rows, slots)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(k), k0) and np.array_equal(bits(v), v0)
+
+
+def test_copy_blocks_bit_exact_and_skips_bad_ids():
+    w = W.custom([100, 64, 33], 16, 8, 128, 16, "bf16", seed=307_071)
+    ref = oracle.run_step(w)
+    k, v = pools_from_oracle(w, ref["k_pool"], ref["v_pool"])
+    used = sorted(set(int(b) for b in w.block_tables.ravel() if b >= 0))
+    free = [b for b in range(w.num_blocks) if b not in used]
+    pairs = np.array([[used[0], free[0]], [used[3], free[1]], [used[5], free[2]],
+                      [-1, free[3]], [used[1], w.num_blocks], [w.num_blocks + 2, free[4]]], np.int64)
+    pa.copy_blocks(k, v, dev(pairs))
+    torch.cuda.synchronize()
+    kb, vb = ref["k_pool"].copy(), ref["v_pool"].copy()
+    oracle.copy_blocks(kb, vb, pairs[:3])
+    assert np.array_equal(bits(k), kb) and np.array_equal(bits(v), vb)
+
+
+def test_slot_mapping_edge_rows():
+    bt = np.array([[3, 9, -1], [4, -1, -1]], np.int32)
+    seq = np.array([0, 0, 0, 1, 1, -1, 2, 0], np.int32)
+    pos = np.array([0, 17, 40, 5, 16, 3, 0, -1], np.int32)
+    got = bits(pa.slot_mapping(dev(bt), dev(seq), dev(pos), 16))
+    want = oracle.slot_mapping(bt, seq, pos, 16)
+    assert want.tolist() == [48, 145, -1, 69, -1, -1, -1, -1]
+    assert np.array_equal(got, want)
+
+
+def test_invalid_block_ids_give_nan_not_faults():
+    """A table entry outside [0, num_blocks) inside ceil(L/B) is a broken
+    precondition: the kernel's bounds check turns that sequence's output into
+    NaN and leaves the others correct."""
+    w = W.custom([50, 50, 50], 8, 2, 128, 16, "bf16", seed=307_081)
+    ref = oracle.run_step(w)
+    k, v = pools_from_oracle(w, ref["k_pool"], ref["v_pool"])
+    bt = w.block_tables.copy()
+    bt[0, 1] = w.num_blocks + 100
+    bt[1, 2] = -1
+    for P in (0, 16):
+        out = as_f64(pa.decode(dev(w.q), k, v, dev(bt), dev(w.context_lens), w.max_context_len,
+                               w.scale, partition_size=P))
+        assert np.isnan(out[0]).all() and np.isnan(out[1]).all()
+        assert np.max(np.abs(out[2] - ref["out"][2])) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------- the five workloads at full size
+
+def test_full_llama3_8b_decode():
+    w = W.llama3_8b_decode()
+    for P in (0, 512):
+        _check_step(w, P, check_pool=(P == 0))
+
+
+def test_full_long_context_split():
+    w = W.long_context()
+    _check_step(w, 512, seqs=range(w.num_seqs), kv_heads=[0, 5], check_pool=False)
+
+
+@pytest.mark.parametrize("phase", ["fork", "steady", "aligned"])
+def test_full_shared_prefix(phase):
+    w = W.shared_prefix(phase)
+    _check_step(w, 512)
+
+
+def test_full_mixed_lengths_block_sweep():
+    outs = {}
+    for B in (8, 16, 32):
+        w = W.mixed_lengths(B)
+        r, _ = _check_step(w, 512, check_pool=(B == 16))
+        outs[B] = bits(r["out"])
+    # same lengths and token data for every B: the outputs agree
+    o8, o16, o32 = (oracle.widen(outs[b], "bf16") for b in (8, 16, 32))
+    assert np.max(np.abs(o8 - o16)) <= TOL["bf16"] and np.max(np.abs(o32 - o16)) <= TOL["bf16"]
