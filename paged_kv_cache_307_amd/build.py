@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
-SOURCES = ["api.hip", "cache_ops.hip", "decode_mfma.hip", "decode_simt.hip"]
+SOURCES = ["api.hip", "cache_ops.hip", "decode_mfma.hip", "decode_simt.hip", "decode_merge.hip"]
 ARCH = "gfx950"
 
 

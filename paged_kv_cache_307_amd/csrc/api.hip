@@ -4,8 +4,39 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
 #include "internal.h"
 #include "pa.h"
+#include "schedule.h"
+
+namespace pa {
+
+int resident_workers(const void* kernel, int block_threads) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::vector<std::tuple<const void*, int, int>> cache;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+      if (std::get<0>(e) == kernel && std::get<1>(e) == dev) return std::get<2>(e);
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess)
+    return 0;
+  const int workers = std::min(kMaxWorkers, std::max(1, cus * per_cu));
+  std::lock_guard<std::mutex> lock(mu);
+  cache.emplace_back(kernel, dev, workers);
+  return workers;
+}
+
+}  // namespace pa
 
 namespace {
 
@@ -50,10 +81,20 @@ int64_t effective_max_len(int32_t max_context_len, int32_t max_blocks_per_seq, i
   return max_context_len < cap ? max_context_len : cap;
 }
 
+int64_t max_parts_for(int64_t max_len, int32_t partition_size) {
+  const int64_t parts = (max_len + partition_size - 1) / partition_size;
+  return parts > 1 ? parts : 1;
+}
+
 int64_t workspace_bytes_for(int32_t num_seqs, int32_t num_kv_heads, int32_t group, int32_t head_dim,
-                            int64_t max_partitions) {
-  return int64_t(num_seqs) * num_kv_heads * max_partitions * pa::record_floats(group, head_dim) *
-         int64_t(sizeof(float));
+                            int64_t max_parts) {
+  return pa::meta_bytes(num_seqs) + pa::max_records(num_seqs, num_kv_heads, max_parts) *
+                                        pa::record_floats(group, head_dim) * int64_t(sizeof(float));
+}
+
+int decode_workers(bool bf16, int head_dim, int block_size) {
+  return bf16 ? pa::decode_workers_bf16_mfma(head_dim, block_size)
+              : pa::decode_workers_simt(head_dim, false);
 }
 
 // Validate the decode arguments and fill the launch plan.  Returns PA_OK with
@@ -82,37 +123,36 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
     return PA_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return PA_ERR_INVALID_ARG;
+  if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
 
   const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
-  const int unit = block_size > 16 ? block_size : 16;
-  int64_t part = partition_size;
-  int64_t max_parts = 1;
-  if (part > 0) {
-    max_parts = max_len > 0 ? (max_len + part - 1) / part : 1;
-  } else {
-    part = max_len > 0 ? ((max_len + unit - 1) / unit) * unit : unit;
-  }
-  if (max_parts <= 1) {
-    max_parts = 1;
-    part = max_len > 0 ? ((max_len + unit - 1) / unit) * unit : unit;
-  }
-  const int64_t grid = int64_t(num_seqs) * num_kv_heads * max_parts;
-  if (grid > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-  plan->split = max_parts > 1;
+  DecodeArgs& a = plan->args;
+  plan->split = partition_size > 0;
   if (plan->split) {
-    const int64_t need = workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, max_parts);
+    const int64_t parts = max_parts_for(max_len, partition_size);
+    const int64_t need = workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts);
     if (!workspace || int64_t(workspace_bytes) < need || !aligned16(workspace))
       return PA_ERR_WORKSPACE;
+    const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size);
+    if (workers <= 0) return PA_ERR_HIP;
+    a.ws_meta = workspace;
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + pa::meta_bytes(num_seqs));
+    a.workers = workers;
+    a.partition_size = partition_size;
+    a.max_partitions = int32_t(parts);
+    a.split = 1;
+  } else {
+    if (int64_t(num_seqs) * num_kv_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+    a.partition_size = int32_t(std::max<int64_t>(16, (max_len + 15) / 16 * 16));
+    a.max_partitions = 1;
+    a.split = 0;
   }
-
-  DecodeArgs& a = plan->args;
   a.out = out;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
-  a.ws = plan->split ? static_cast<float*>(workspace) : nullptr;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;
@@ -120,8 +160,6 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = int32_t(max_len);
-  a.partition_size = int32_t(part);
-  a.max_partitions = int32_t(max_parts);
   a.scale_log2e = scale * 1.4426950408889634f;
   plan->head_dim = head_dim;
   plan->block_size = block_size;
@@ -199,10 +237,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
                                  int32_t head_dim, int32_t max_context_len,
                                  int32_t partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_context_len <= 0 || partition_size <= 0 || num_heads % num_kv_heads != 0)
+      max_context_len < 0 || partition_size <= 0 || num_heads % num_kv_heads != 0)
     return 0;
-  const int64_t parts = (int64_t(max_context_len) + partition_size - 1) / partition_size;
-  if (parts <= 1) return 0;
+  const int64_t parts = max_parts_for(max_context_len, partition_size);
   return size_t(workspace_bytes_for(num_seqs, num_kv_heads, num_heads / num_kv_heads, head_dim, parts));
 }
 
@@ -234,19 +271,25 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
   if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
     return PA_ERR_INVALID_ARG;
   if (num_seqs == 0 || partition_size == 0) return PA_OK;
-  const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
-  const int64_t parts = max_len > 0 ? (max_len + partition_size - 1) / partition_size : 1;
-  if (parts <= 1) return PA_OK;
   if (!out || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out)) return PA_ERR_INVALID_ARG;
+  const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
+  const int64_t parts = max_parts_for(max_len, partition_size);
   const int32_t group = num_heads / num_kv_heads;
   if (!workspace || !aligned16(workspace) ||
       int64_t(workspace_bytes) < workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts))
     return PA_ERR_WORKSPACE;
-  if (int64_t(num_seqs) * num_kv_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size);
+  if (workers <= 0) return PA_ERR_HIP;
   DecodeArgs a{};
   a.out = out;
   a.context_lens = context_lens;
-  a.ws = static_cast<float*>(const_cast<void*>(workspace));
+  a.ws_meta = const_cast<void*>(workspace);
+  a.ws = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
+                                  pa::meta_bytes(num_seqs));
+  a.workers = workers;
+  a.split = 1;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.num_kv_heads = num_kv_heads;

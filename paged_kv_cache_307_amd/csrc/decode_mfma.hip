@@ -44,6 +44,7 @@
 #include <math.h>
 
 #include "device_common.h"
+#include "schedule.h"
 
 namespace pa {
 
@@ -55,8 +56,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kThreads = 64;  // one wave per worker
 constexpr int kTile = 16;
 constexpr float kRescaleThreshold = 8.0f;
 
@@ -64,267 +64,283 @@ template <int D>
 struct Tile {
   uint4 k[D / 32];
   uint2 v[D / 16];
+  bool bad;  // a block id outside [0, num_blocks): the tile's results become NaN
 };
 
-// Physical placement of one 16-token tile for this lane.
-struct TilePlace {
-  const char* k_base;  // wave-uniform when B >= 16
-  const char* v_base;
-  bool bad;            // a block id outside [0, num_blocks): results become NaN
+// Physical block ids of one tile (wave-uniform scalars).  A tile is one
+// block when B >= 16 and two consecutive blocks when B == 8.
+struct TileIds {
+  int pb0;
+  int pb1;
 };
+
+template <int B>
+__device__ __forceinline__ TileIds fetch_ids(const int32_t* row, int t0, int nblk) {
+  const int lb = t0 / B;
+  TileIds id;
+  id.pb0 = load_ro(row, lb);
+  if constexpr (B < kTile) {
+    id.pb1 = (lb + 1 < nblk) ? load_ro(row, lb + 1) : id.pb0;
+  } else {
+    id.pb1 = id.pb0;
+  }
+  return id;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
   float2_t f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data
+// format, no swizzle; the loads below are untyped 16- and 8-byte fetches.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRawBufferWord3);
+}
+
+// Issue the loads of one tile.  B >= 16: the tile lies in one block; its K
+// and V bases are scalars and each lane adds a fixed 32-bit offset (buffer
+// loads, bounds-checked against the tile).  B == 8: each lane picks the
+// block its rows fall in and uses a 64-bit address.
 template <int D, int B>
-__device__ __forceinline__ TilePlace place_tile(const DecodeArgs& a, const int32_t* row, int kvh,
-                                                int t0, int nblk, int lane) {
-  constexpr int64_t kTileBytes = int64_t(B) * D * 2;  // one (block, KV head) tile
+__device__ __forceinline__ void load_tile(Tile<D>& r, const DecodeArgs& a, const TileIds& id,
+                                          int kvh, int t0, int lane, uint32_t k_off,
+                                          uint32_t v_off) {
+  constexpr int kTileBytes = B * D * 2;  // one (block, KV head) tile of K or of V
   const char* kc = static_cast<const char*>(a.k_cache);
   const char* vc = static_cast<const char*>(a.v_cache);
-  TilePlace tp;
   if constexpr (B >= kTile) {
-    const int lb = t0 / B;
-    int pb = row[lb];
-    tp.bad = unsigned(pb) >= unsigned(a.num_blocks);
-    pb = tp.bad ? 0 : pb;
-    const int64_t tile = int64_t(pb) * a.num_kv_heads + kvh;
+    const bool bad = unsigned(id.pb0) >= unsigned(a.num_blocks);
+    const int pb = bad ? 0 : id.pb0;
+    const int64_t tile = (int64_t(pb) * a.num_kv_heads + kvh) * kTileBytes;
     const int in_block = t0 % B;  // 0, or 16 when B == 32
-    tp.k_base = kc + tile * kTileBytes + int64_t(in_block) * D * 2;
-    tp.v_base = vc + tile * kTileBytes + int64_t(in_block) * 2;
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + tile + in_block * D * 2, kTileBytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + tile + in_block * 2, kTileBytes);
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j)
+      r.k[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * j, 0));
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      r.v[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 32 * B * c, 0));
+    r.bad = bad;
   } else {
-    // B == 8: the tile spans two blocks; the second may not exist.
-    const int lb0 = t0 / B;
-    int pb0 = row[lb0];
-    int pb1 = (lb0 + 1 < nblk) ? row[lb0 + 1] : pb0;
-    const bool bad0 = unsigned(pb0) >= unsigned(a.num_blocks);
-    const bool bad1 = unsigned(pb1) >= unsigned(a.num_blocks);
-    pb0 = bad0 ? 0 : pb0;
-    pb1 = bad1 ? 0 : pb1;
+    const bool bad0 = unsigned(id.pb0) >= unsigned(a.num_blocks);
+    const bool bad1 = unsigned(id.pb1) >= unsigned(a.num_blocks);
+    const int pb0 = bad0 ? 0 : id.pb0;
+    const int pb1 = bad1 ? 0 : id.pb1;
     // K: this lane's token is (lane & 15); V: its tokens are 4*(lane >> 4) ..
     const bool k_second = (lane & 15) >= B;
     const bool v_second = (lane >> 4) >= 2;
-    const int64_t tk = int64_t(k_second ? pb1 : pb0) * a.num_kv_heads + kvh;
-    const int64_t tv = int64_t(v_second ? pb1 : pb0) * a.num_kv_heads + kvh;
-    tp.k_base = kc + tk * kTileBytes - (k_second ? int64_t(B) * D * 2 : 0);
-    tp.v_base = vc + tv * kTileBytes - (v_second ? int64_t(B) * 2 : 0);
-    tp.bad = (lane >> 4) >= 2 ? bad1 : bad0;  // the S^T rows this lane owns
+    const int64_t tk = (int64_t(k_second ? pb1 : pb0) * a.num_kv_heads + kvh) * kTileBytes;
+    const int64_t tv = (int64_t(v_second ? pb1 : pb0) * a.num_kv_heads + kvh) * kTileBytes;
+    const char* kb = kc + tk - (k_second ? B * D * 2 : 0) + k_off;
+    const char* vb = vc + tv - (v_second ? B * 2 : 0) + v_off;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) r.k[j] = *reinterpret_cast<const uint4*>(kb + 64 * j);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) r.v[c] = *reinterpret_cast<const uint2*>(vb + 32 * B * c);
+    r.bad = v_second ? bad1 : bad0;  // the S^T rows this lane owns
   }
-  return tp;
 }
 
-template <int D, int B>
-__device__ __forceinline__ void load_tile(Tile<D>& r, const TilePlace& tp, uint32_t k_off,
-                                          uint32_t v_off) {
-#pragma unroll
-  for (int j = 0; j < D / 32; ++j)
-    r.k[j] = *reinterpret_cast<const uint4*>(tp.k_base + k_off + 64 * j);
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    r.v[c] = *reinterpret_cast<const uint2*>(tp.v_base + v_off + 32 * B * c);
+// x and its values in lanes l ^ 16, l ^ 32, l ^ 48 (the four row groups of
+// an MFMA result column), combined with max or +, via gfx950 lane swaps.
+__device__ __forceinline__ float colmax4(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float colsum4(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-template <int D, int B>
-__global__ __launch_bounds__(kThreads) void decode_bf16_mfma_kernel(DecodeArgs a) {
+template <int D, int B, bool kSplit>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : (B >= kTile ? 3 : 2))))
+void decode_bf16_mfma_kernel(DecodeArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int DCH = D / 16;
-
-  const int bid = blockIdx.x;
-  const int p = bid % a.max_partitions;
-  const int sg = bid / a.max_partitions;
-  const int kvh = sg % a.num_kv_heads;
-  const int s = sg / a.num_kv_heads;
   const int G = a.group;
-  const int L = effective_len(a, s, B);
-  const int P = a.partition_size;
-  const int nparts = (L + P - 1) / P;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = wave_uniform(tid >> 6);
+  const int lane = threadIdx.x;
   const int col = lane & 15;
   const int grp = lane >> 4;
   uint16_t* out = static_cast<uint16_t*>(a.out);
-
-  if (L == 0) {
-    if (p == 0) {
-      uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G) * D;
-      for (int i = tid; i < G * D; i += kThreads) o[i] = 0;
-    }
-    return;
-  }
-  if (p >= nparts) return;
-
-  const int t_begin = p * P;
-  const int t_end = min(L, t_begin + P);
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  const int nblk = (L + B - 1) / B;
-  const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
-
-  // Q^T operand: column col = query head kvh*G + col (zero beyond G).
-  bf16x8_t qop[KSTEPS];
-  {
-    const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
-                         (int64_t(s) * a.num_heads + int64_t(kvh) * G + col) * D + 8 * grp;
-#pragma unroll
-    for (int j = 0; j < KSTEPS; ++j) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col < G) v = *reinterpret_cast<const uint4*>(qh + 32 * j);
-      qop[j] = __builtin_bit_cast(bf16x8_t, v);
-    }
-  }
 
   // Per-lane byte offsets inside a tile.
   const uint32_t k_off = uint32_t(col) * D * 2 + uint32_t(grp) * 16;
   const uint32_t v_off = uint32_t(col) * B * 2 + uint32_t(grp) * 8;
 
-  floatx4_t acc[DCH];
-#pragma unroll
-  for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  // One piece: tiles [tin, tin + ntile) of pair (s, kvh).
+  auto piece = [&](int s, int kvh, int L, int tin, int ntile, bool whole, int64_t rec_index) {
+    // Every argument is the same in all lanes; say so, so that addresses
+    // built from them stay in scalar registers.
+    s = wave_uniform(s);
+    kvh = wave_uniform(kvh);
+    L = wave_uniform(L);
+    tin = wave_uniform(tin);
+    ntile = wave_uniform(ntile);
+    whole = wave_uniform(int(whole)) != 0;
+    rec_index = wave_uniform64(rec_index);
+    const int t_begin = tin * kTile;
+    const int t_end = min(L, (tin + ntile) * kTile);
+    const int nblk = (L + B - 1) / B;
+    const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
 
-  auto consume = [&](Tile<D>& r, int tile, bool bad) {
-    const int t0 = t_begin + tile * kTile;
-    const int valid = t_end - t0;  // >= 1
-    floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    // Q^T operand: column col = query head kvh*G + col (zero beyond G).
+    bf16x8_t qop[KSTEPS];
+    {
+      const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                           (int64_t(s) * a.num_heads + int64_t(kvh) * G + col) * D + 8 * grp;
 #pragma unroll
-    for (int j = 0; j < KSTEPS; ++j)
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]), qop[j],
-                                                     sacc, 0, 0, 0);
-    float x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
-    if (valid < kTile) {  // last, partial tile: drop tokens >= t_end
-      const int first = 4 * grp;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = (first + i < valid) ? x[i] : -INFINITY;
-      const int n = min(max(valid - first, 0), 4);
-      const uint32_t mx = (n >= 1 ? 0x0000FFFFu : 0u) | (n >= 2 ? 0xFFFF0000u : 0u);
-      const uint32_t my = (n >= 3 ? 0x0000FFFFu : 0u) | (n >= 4 ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int c = 0; c < DCH; ++c) {
-        r.v[c].x &= mx;
-        r.v[c].y &= my;
+      for (int j = 0; j < KSTEPS; ++j) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col < G) v = *reinterpret_cast<const uint4*>(qh + 32 * j);
+        qop[j] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
-    if (bad) {
+
+    floatx4_t acc[DCH];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
+    for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    auto t0_of = [&](int k) { return t_begin + k * kTile; };
+
+    auto consume = [&](Tile<D>& r, int k) {
+      const int valid = t_end - t0_of(k);  // >= 1
+      floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
+                                                       qop[j], sacc, 0, 0, 0);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
+      if (valid < kTile) {  // last, partial tile: drop tokens >= t_end
+        const int first = 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (first + i < valid) ? x[i] : -INFINITY;
+        const int n = min(max(valid - first, 0), 4);
+        const uint32_t mx = (n >= 1 ? 0x0000FFFFu : 0u) | (n >= 2 ? 0xFFFF0000u : 0u);
+        const uint32_t my = (n >= 3 ? 0x0000FFFFu : 0u) | (n >= 4 ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < DCH; ++c) {
+          r.v[c].x &= mx;
+          r.v[c].y &= my;
+        }
+      }
+      if (r.bad) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
+      }
+      const float tmax = colmax4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      if (__any(tmax > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < DCH; ++c) acc[c] *= alpha;
+        m_run = m_new;
+      }
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const uint2 pp = make_uint2(pack_bf16x2_rne(pr[0], pr[1]), pack_bf16x2_rne(pr[2], pr[3]));
+      const short4_t pop = __builtin_bit_cast(short4_t, pp);
+#pragma unroll
+      for (int c = 0; c < DCH; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, r.v[c]),
+                                                           pop, acc[c], 0, 0, 0);
+    };
+
+    // Software pipeline over the piece's tiles: while tile k is consumed the
+    // loads of tile k+1 are in flight and the block ids of tile k+2 are
+    // being fetched.  The loads are issued unconditionally (past the last
+    // tile they repeat it, and the caches serve the repeat), so the wait
+    // before each tile covers exactly the loads issued before it.
+    {
+      Tile<D> r0, r1;
+      const int last = ntile - 1;
+      TileIds id = fetch_ids<B>(row, t0_of(0), nblk);
+      load_tile<D, B>(r0, a, id, kvh, t0_of(0), lane, k_off, v_off);
+      id = fetch_ids<B>(row, t0_of(min(1, last)), nblk);
+      for (int k = 0; k < ntile; k += 2) {
+        load_tile<D, B>(r1, a, id, kvh, t0_of(min(k + 1, last)), lane, k_off, v_off);
+        id = fetch_ids<B>(row, t0_of(min(k + 2, last)), nblk);
+        __builtin_amdgcn_sched_barrier(0);  // keep the id fetch ahead of this tile's math
+        consume(r0, k);
+        if (k + 1 >= ntile) break;
+        load_tile<D, B>(r0, a, id, kvh, t0_of(min(k + 2, last)), lane, k_off, v_off);
+        id = fetch_ids<B>(row, t0_of(min(k + 3, last)), nblk);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(r1, k + 1);
+      }
     }
-    float tmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    if (__any(tmax > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+
+    // l over the four row groups of each column; every lane of a column
+    // then holds the column's (m, l).
+    const float l_tot = colsum4(l_run);
+    if (col < G) {
+      if (whole) {
+        const float inv_l = 1.0f / l_tot;
+        uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G + col) * D + 4 * grp;
 #pragma unroll
-      for (int c = 0; c < DCH; ++c) acc[c] *= alpha;
-      m_run = m_new;
+        for (int c = 0; c < DCH; ++c)
+          *reinterpret_cast<uint2*>(o + 16 * c) =
+              make_uint2(pack_bf16x2_rne(acc[c][0] * inv_l, acc[c][1] * inv_l),
+                         pack_bf16x2_rne(acc[c][2] * inv_l, acc[c][3] * inv_l));
+      } else {
+        float* rec = a.ws + rec_index * record_floats(G, D);
+#pragma unroll
+        for (int c = 0; c < DCH; ++c)
+          *reinterpret_cast<floatx4_t*>(rec + col * D + 16 * c + 4 * grp) = acc[c];
+        if (grp == 0) {
+          rec[G * D + col] = m_run;
+          rec[G * D + G + col] = l_tot;
+        }
+      }
     }
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_run);
-    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    const uint2 pp = make_uint2(pack_bf16x2_rne(pr[0], pr[1]), pack_bf16x2_rne(pr[2], pr[3]));
-    const short4_t pop = __builtin_bit_cast(short4_t, pp);
-#pragma unroll
-    for (int c = 0; c < DCH; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, r.v[c]), pop,
-                                                         acc[c], 0, 0, 0);
   };
 
-  // Software pipeline: tile i+4's loads are in flight while tile i is used.
-  Tile<D> r0, r1;
-  int tile = wave;
-  bool bad0 = false, bad1 = false;
-  if (tile < ntiles) {
-    TilePlace tp = place_tile<D, B>(a, row, kvh, t_begin + tile * kTile, nblk, lane);
-    bad0 = tp.bad;
-    load_tile<D, B>(r0, tp, k_off, v_off);
-  }
-  while (tile < ntiles) {
-    int next = tile + kWaves;
-    if (next < ntiles) {
-      TilePlace tp = place_tile<D, B>(a, row, kvh, t_begin + next * kTile, nblk, lane);
-      bad1 = tp.bad;
-      load_tile<D, B>(r1, tp, k_off, v_off);
+  if constexpr (kSplit) {
+    walk_slice(a, B, lane, blockIdx.x, piece);
+  } else {
+    // one worker per (sequence, KV head); consecutive workers are the KV
+    // heads of one sequence (workgroup i runs on XCD i % 8)
+    const int kvh = blockIdx.x % a.num_kv_heads;
+    const int s = blockIdx.x / a.num_kv_heads;
+    const int L = effective_len(a, s, B);
+    if (L == 0) {
+      uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G) * D;
+      for (int i = lane; i < G * D; i += kThreads) o[i] = 0;
+      return;
     }
-    consume(r0, tile, bad0);
-    tile = next;
-    if (tile >= ntiles) break;
-    next = tile + kWaves;
-    if (next < ntiles) {
-      TilePlace tp = place_tile<D, B>(a, row, kvh, t_begin + next * kTile, nblk, lane);
-      bad0 = tp.bad;
-      load_tile<D, B>(r0, tp, k_off, v_off);
-    }
-    consume(r1, tile, bad1);
-    tile = next;
-  }
-
-  // Wave totals: l over the four row groups of each column.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-
-  // Combine the 4 waves in LDS.
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ floatx4_t sm_acc[kWaves][DCH][64];
-  if (grp == 0) {
-    sm_m[wave][col] = m_run;
-    sm_l[wave][col] = l_run;
-  }
-#pragma unroll
-  for (int c = 0; c < DCH; ++c) sm_acc[wave][c][lane] = acc[c];
-  __syncthreads();
-
-  float M = sm_m[0][col];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][col]);
-  float wgt[kWaves];
-  float l_tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sm_m[w][col];
-    wgt[w] = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    l_tot += wgt[w] * sm_l[w][col];
-  }
-
-  const bool single = nparts == 1;
-  const int h = kvh * G + col;
-  float* rec = nullptr;
-  if (!single)
-    rec = a.ws + ((int64_t(s) * a.num_kv_heads + kvh) * a.max_partitions + p) * record_floats(G, D);
-  if (!single && wave == 0 && grp == 0 && col < G) {
-    rec[G * D + col] = M;
-    rec[G * D + G + col] = l_tot;
-  }
-  const float inv_l = 1.0f / l_tot;
-  for (int c = wave; c < DCH; c += kWaves) {
-    floatx4_t o = wgt[0] * sm_acc[0][c][lane];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) o += wgt[w] * sm_acc[w][c][lane];
-    if (col < G) {
-      const int d0 = 16 * c + 4 * grp;
-      if (single) {
-        const uint2 ob = make_uint2(pack_bf16x2_rne(o[0] * inv_l, o[1] * inv_l),
-                                    pack_bf16x2_rne(o[2] * inv_l, o[3] * inv_l));
-        *reinterpret_cast<uint2*>(out + (int64_t(s) * a.num_heads + h) * D + d0) = ob;
-      } else {
-        *reinterpret_cast<floatx4_t*>(rec + col * D + d0) = o;
-      }
-    }
+    piece(s, kvh, L, 0, (L + kTile - 1) / kTile, true, 0);
   }
 }
 
 template <int D, int B>
 hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t grid = int64_t(a.num_seqs) * a.num_kv_heads * a.max_partitions;
-  return launch(decode_bf16_mfma_kernel<D, B>, dim3(unsigned(grid)), dim3(kThreads), 0, stream, a);
+  if (a.split)
+    return launch(decode_bf16_mfma_kernel<D, B, true>, dim3(unsigned(a.workers)), dim3(kThreads), 0,
+                  stream, a);
+  const int64_t grid = int64_t(a.num_seqs) * a.num_kv_heads;
+  return launch(decode_bf16_mfma_kernel<D, B, false>, dim3(unsigned(grid)), dim3(kThreads), 0,
+                stream, a);
+}
+
+template <int D, int B>
+int workers_one() {
+  return resident_workers(reinterpret_cast<const void*>(decode_bf16_mfma_kernel<D, B, true>),
+                          kThreads);
 }
 
 template <int D>
@@ -337,6 +353,16 @@ hipError_t launch_d(const DecodeArgs& a, int block_size, hipStream_t stream) {
   }
 }
 
+template <int D>
+int workers_d(int block_size) {
+  switch (block_size) {
+    case 8: return workers_one<D, 8>();
+    case 16: return workers_one<D, 16>();
+    case 32: return workers_one<D, 32>();
+    default: return 0;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_size,
@@ -346,6 +372,15 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_
     case 128: return launch_d<128>(a, block_size, stream);
     case 256: return launch_d<256>(a, block_size, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+int decode_workers_bf16_mfma(int head_dim, int block_size) {
+  switch (head_dim) {
+    case 64: return workers_d<64>(block_size);
+    case 128: return workers_d<128>(block_size);
+    case 256: return workers_d<256>(block_size);
+    default: return 0;
   }
 }
 

@@ -18,7 +18,9 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws;                  // split-KV records, nullptr when max_partitions == 1
+  float* ws;                  // split-KV records (see schedule.h), nullptr in single pass
+  void* ws_meta;              // split-KV meta block: prefT, prefP, N
+  int32_t workers;            // split-KV worker grid
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
@@ -28,6 +30,7 @@ struct DecodeArgs {
   int32_t max_context_len;    // clamp for context_lens
   int32_t partition_size;     // tokens per partition (multiple of 16 and of B)
   int32_t max_partitions;     // ceil(max_context_len / partition_size), >= 1
+  int32_t split;              // 1: balanced split-KV workers; 0: one wave per (seq, KV head)
   float scale_log2e;          // scale * log2(e)
 };
 
@@ -70,6 +73,12 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
 // with no compiled kernel (the API checks shapes first).
 hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_size,
                                    hipStream_t stream);
+// Number of split-KV workers a decode kernel should use on the current
+// device: resident workgroups per compute unit x compute units, capped at
+// the workspace's worker bound.  0 on failure.  Cached per kernel and device.
+int resident_workers(const void* kernel, int block_threads);
+int decode_workers_bf16_mfma(int head_dim, int block_size);
+int decode_workers_simt(int head_dim, bool bf16);
 hipError_t launch_decode_simt(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
                               hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int block_size, bool bf16,

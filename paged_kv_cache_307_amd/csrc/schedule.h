@@ -1,0 +1,199 @@
+// Work schedule of the split-KV decode: a balanced cut of all KV tiles over
+// a fixed number of single-wave workers.
+//
+// Every (sequence s, KV head g) owns T_s = ceil(L_s / 16) tiles of 16 tokens.
+// The tiles of all pairs are laid on one line in (s, g, tile) order; pair
+// (s, g) starts at Hkv * prefT[s] + g * T_s, prefT being the exclusive prefix
+// sum of T_s.  Worker b of W owns the line slice [start(b), start(b+1)) with
+// start(b) = floor(N * b / W), N the line length, so every worker streams the
+// same number of tiles and all finish together.
+//
+// A worker cuts its slice into pieces at pair boundaries and at partition
+// boundaries (every partition_size tokens of a pair).  Each piece yields one
+// log-sum-exp record, stored at index  gp + b,  gp being the global index of
+// the partition the piece lies in (partitions numbered along the line, pair
+// (s, g) starting at Hkv * prefP[s] + g * nparts_s, prefP the exclusive
+// prefix of nparts_s = ceil(L_s / partition_size)).  Along the line every
+// cut raises gp or b (or both), so indices are distinct and below
+// total_partitions + W.  A piece that is a whole pair writes the final
+// output instead of a record.  The merge walks the same cuts per pair.
+#pragma once
+
+#include "device_common.h"
+
+namespace pa {
+
+// Largest worker grid the workspace is sized for.
+constexpr int kMaxWorkers = 4096;
+
+// Workspace layout (bytes): int32 prefT[S], int32 prefP[S], int64 N (at
+// an 8-aligned offset), padding to 256, then the float records.
+__host__ __device__ inline int64_t meta_bytes(int num_seqs) {
+  const int64_t n_off = (int64_t(num_seqs) * 8 + 7) / 8 * 8;
+  return (n_off + 8 + 255) / 256 * 256;
+}
+__host__ __device__ inline int64_t max_records(int num_seqs, int num_kv_heads, int64_t max_parts) {
+  return int64_t(num_seqs) * num_kv_heads * max_parts + kMaxWorkers;
+}
+
+__device__ __forceinline__ int64_t slice_start(int64_t n, int workers, int b) {
+  return n * b / workers;
+}
+// The worker whose slice holds line position x (0 <= x < n).
+__device__ __forceinline__ int owner_of(int64_t n, int workers, int64_t x) {
+  return int(((x + 1) * workers - 1) / n);
+}
+
+struct PairShape {
+  int tiles;   // T_s
+  int parts;   // nparts_s
+};
+
+__device__ __forceinline__ PairShape pair_shape(const DecodeArgs& a, int s, int block_size) {
+  const int L = effective_len(a, s, block_size);
+  PairShape p;
+  p.tiles = (L + 15) / 16;
+  p.parts = (L + a.partition_size - 1) / a.partition_size;
+  return p;
+}
+
+// Inclusive wave-wide prefix sum of a 32-bit value.
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// One wave locates worker b's slice: N (the line length), [x0, x1), and the
+// sequence holding x0 with its prefixes.  Worker 0 also publishes prefT,
+// prefP and N in the workspace meta block for the merge.
+struct Slice {
+  int64_t n, x0, x1;
+  int seq;          // sequence holding x0 (valid when x0 < x1)
+  int64_t pref_t;   // prefT[seq]
+  int64_t pref_p;   // prefP[seq]
+};
+
+__device__ __forceinline__ int64_t* meta_n(const DecodeArgs& a) {
+  return reinterpret_cast<int64_t*>(reinterpret_cast<char*>(a.ws_meta) +
+                                    (int64_t(a.num_seqs) * 8 + 7) / 8 * 8);
+}
+
+__device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_size, int lane, int b) {
+  const int S = a.num_seqs;
+  const int per = (S + 63) / 64;  // consecutive sequences per lane
+  const int first = min(S, lane * per);
+  const int last = min(S, first + per);
+  int lt = 0, lp = 0;
+  for (int s = first; s < last; ++s) {
+    const PairShape ps = pair_shape(a, s, block_size);
+    lt += ps.tiles;
+    lp += ps.parts;
+  }
+  const int it = wave_inclusive_scan(lt, lane);
+  const int ip = wave_inclusive_scan(lp, lane);
+  Slice r;
+  r.n = int64_t(wave_uniform(__shfl(it, 63))) * a.num_kv_heads;
+  r.x0 = r.n > 0 ? slice_start(r.n, a.workers, b) : 0;
+  r.x1 = r.n > 0 ? slice_start(r.n, a.workers, b + 1) : 0;
+  const bool publish = b == 0;
+  int32_t* meta = reinterpret_cast<int32_t*>(a.ws_meta);
+  int found_s = -1;
+  int64_t found_t = 0, found_p = 0;
+  int64_t ct = it - lt, cp = ip - lp;
+  for (int s = first; s < last; ++s) {
+    const PairShape ps = pair_shape(a, s, block_size);
+    if (publish) {
+      meta[s] = int32_t(ct);
+      meta[S + s] = int32_t(cp);
+    }
+    if (ps.tiles > 0 && r.x0 >= ct * a.num_kv_heads && r.x0 < (ct + ps.tiles) * a.num_kv_heads) {
+      found_s = s;
+      found_t = ct;
+      found_p = cp;
+    }
+    ct += ps.tiles;
+    cp += ps.parts;
+  }
+  if (publish && lane == 0) *meta_n(a) = r.n;
+  const unsigned long long owner = __ballot(found_s >= 0);
+  const int src = owner ? int(__builtin_ctzll(owner)) : 0;
+  r.seq = wave_uniform(__shfl(found_s, src));
+  r.pref_t = wave_uniform64(__shfl(found_t, src));
+  r.pref_p = wave_uniform64(__shfl(found_p, src));
+  return r;
+}
+
+// Calls piece(s, g, L, first_tile, num_tiles, whole, record_index) for
+// every piece of worker b's slice, in line order.
+template <typename PieceFn>
+__device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, int lane, int b,
+                                           PieceFn&& piece) {
+  const Slice sl = locate_slice(a, block_size, lane, b);
+  if (sl.x0 >= sl.x1) return;
+  const int Hkv = a.num_kv_heads;
+  const int tpp = a.partition_size / 16;  // tiles per partition
+  int s = sl.seq;
+  int64_t sbase = sl.pref_t * Hkv;        // line start of sequence s
+  int64_t gpb = sl.pref_p * Hkv;          // first partition index of sequence s
+  PairShape ps = pair_shape(a, s, block_size);
+  int64_t cur = sl.x0;
+  while (cur < sl.x1) {
+    if (cur >= sbase + int64_t(Hkv) * ps.tiles) {
+      sbase += int64_t(Hkv) * ps.tiles;
+      gpb += int64_t(Hkv) * ps.parts;
+      ++s;
+      ps = pair_shape(a, s, block_size);
+      continue;
+    }
+    const int64_t off = cur - sbase;
+    const int g = int(off / ps.tiles);
+    const int tin = int(off - int64_t(g) * ps.tiles);
+    const int part = tin / tpp;
+    int64_t end = sbase + int64_t(g + 1) * ps.tiles;
+    end = min(end, sbase + int64_t(g) * ps.tiles + int64_t(part + 1) * tpp);
+    end = min(end, sl.x1);
+    const int ntile = int(end - cur);
+    const bool whole = tin == 0 && ntile == ps.tiles;
+    const int64_t rec = gpb + int64_t(g) * ps.parts + part + b;
+    piece(s, g, effective_len(a, s, block_size), tin, ntile, whole, rec);
+    cur = end;
+  }
+}
+
+// Calls fn(record_index) for every piece of pair (s, g) in line order and
+// returns the number of pieces.  Needs the meta block written by worker 0.
+template <typename Fn>
+__device__ __forceinline__ int for_each_piece(const DecodeArgs& a, int block_size, int s, int g,
+                                              Fn&& fn) {
+  const PairShape ps = pair_shape(a, s, block_size);
+  if (ps.tiles == 0) return 0;
+  const int32_t* meta = reinterpret_cast<const int32_t*>(a.ws_meta);
+  const int64_t n = *meta_n(a);
+  const int Hkv = a.num_kv_heads;
+  const int tpp = a.partition_size / 16;
+  const int64_t base = int64_t(meta[s]) * Hkv + int64_t(g) * ps.tiles;
+  const int64_t gp0 = int64_t(meta[a.num_seqs + s]) * Hkv + int64_t(g) * ps.parts;
+  const int64_t stop = base + ps.tiles;
+  int b = owner_of(n, a.workers, base);
+  int64_t cut = slice_start(n, a.workers, b + 1);
+  int64_t cur = base;
+  int count = 0;
+  while (cur < stop) {
+    while (cur >= cut) {
+      ++b;
+      cut = slice_start(n, a.workers, b + 1);
+    }
+    const int part = int((cur - base) / tpp);
+    const int64_t end = min(min(stop, cut), base + int64_t(part + 1) * tpp);
+    fn(gp0 + part + b);
+    ++count;
+    cur = end;
+  }
+  return count;
+}
+
+}  // namespace pa

@@ -90,9 +90,11 @@ def test_merge_rejects_before_launch(lib):
     assert m(FAKE, FAKE, 4, 30, 8, 128, 64, 16, 1024, 512, FAKE, 1 << 30, BF16, None) == INVALID
     assert m(FAKE, FAKE, 4, 32, 8, 96, 64, 16, 1024, 512, FAKE, 1 << 30, BF16, None) == UNSUPPORTED
     assert m(FAKE, FAKE, 4, 32, 8, 128, 64, 16, 1024, 512, None, 0, BF16, None) == WORKSPACE
-    # single partition or no split: nothing to merge, no launch
-    assert m(FAKE, FAKE, 4, 32, 8, 128, 64, 16, 512, 512, None, 0, BF16, None) == OK
+    # split mode always reads the workspace, even for a single partition
+    assert m(FAKE, FAKE, 4, 32, 8, 128, 64, 16, 512, 512, None, 0, BF16, None) == WORKSPACE
+    # no split (partition_size 0) or no sequences: nothing to merge, no launch
     assert m(FAKE, FAKE, 4, 32, 8, 128, 64, 16, 1024, 0, None, 0, BF16, None) == OK
+    assert m(FAKE, FAKE, 0, 32, 8, 128, 64, 16, 1024, 512, None, 0, BF16, None) == OK
 
 
 def test_write_and_copy_reject_before_launch(lib):
@@ -116,15 +118,17 @@ def test_write_and_copy_reject_before_launch(lib):
 
 
 def test_workspace_size_formula(lib):
-    # record = o[G][D] + m[G] + l[G] padded to a multiple of 4 floats
+    # meta block (int32 prefT[S], prefP[S], int64 N, padded to 256 bytes), then
+    # S*Hkv*max(1, ceil(L/P)) + 4096 records of o[G][D], m[G], l[G] padded
+    # to a multiple of 4 floats
     def expect(S, Hq, Hkv, D, L, P):
         G = Hq // Hkv
-        parts = -(-L // P)
-        if parts <= 1:
-            return 0
+        parts = max(1, -(-L // P))
         rec = G * D + 4 * ((G + 1) // 2)
-        return S * Hkv * parts * rec * 4
+        meta = ((S * 8 + 7) // 8 * 8 + 8 + 255) // 256 * 256
+        return meta + (S * Hkv * parts + 4096) * rec * 4
     for args in [(64, 32, 8, 128, 4096, 512), (8, 32, 8, 128, 131072, 512), (3, 5, 5, 64, 100, 16),
                  (256, 64, 8, 128, 8192, 512), (4, 32, 8, 128, 512, 512), (2, 4, 2, 64, 0, 16)]:
         assert pa.decode_workspace_bytes(*args) == expect(*args), args
     assert pa.decode_workspace_bytes(4, 30, 8, 128, 1024, 512) == 0
+    assert pa.decode_workspace_bytes(4, 32, 8, 128, 1024, 0) == 0

@@ -129,7 +129,7 @@ def test_write_skips_negative_and_out_of_range_slots():
 
 
 def test_copy_blocks_bit_exact_and_skips_bad_ids():
-    w = W.custom([100, 64, 33], 16, 8, 128, 16, "bf16", seed=307_071)
+    w = W.custom([100, 64, 33], 16, 8, 128, 16, "bf16", seed=307_071, pool_factor=2.0)
     ref = oracle.run_step(w)
     k, v = pools_from_oracle(w, ref["k_pool"], ref["v_pool"])
     used = sorted(set(int(b) for b in w.block_tables.ravel() if b >= 0))
