@@ -94,6 +94,24 @@ def cpu_baseline(w, budget_s=12.0):
                       f"same workload, single thread, {el:.1f} s"}
 
 
+def copy_calibration(pairs=2048, reps=5):
+    """Run pa_copy_blocks on a known number of bytes (for scaling the HBM
+    byte counters of a profiler: each launch reads and writes
+    pairs * 2 pools * 32 KiB)."""
+    import torch
+
+    import paged_kv_cache_307_amd as pa
+    dev = torch.device("cuda", 0)
+    k, v = pa.empty_kv_cache(2 * pairs, 8, 16, 128, torch.bfloat16, dev, fill=1.0)
+    m = torch.stack([torch.arange(pairs), torch.arange(pairs) + pairs], 1).to(dev)
+    for _ in range(reps):
+        pa.copy_blocks(k, v, m)
+    torch.cuda.synchronize()
+    block = 8 * 16 * 128 * 2
+    print(json.dumps({"copy_calibration": {"launches": reps, "read_bytes_per_launch": pairs * 2 * block,
+                                           "write_bytes_per_launch": pairs * 2 * block}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,10 +121,15 @@ def main():
     ap.add_argument("--partition", type=int, default=512)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run pa_copy_blocks on a known byte count (profiler calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     w = make_workload(args.workload)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)

@@ -142,20 +142,23 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
                    int32_t dtype, void* stream);
 
 /*
- * Split-KV workspace.  A context of length L is split into partitions of
- * partition_size tokens, partition p holding tokens
- * [p * partition_size, min((p + 1) * partition_size, L)).  Each partition
- * yields one record per (sequence, KV head) of
- *   float o[G][head_dim], m[G], l[G]      (G = num_heads / num_kv_heads)
- * padded to R = G * head_dim + 4 * ceil(G / 2) floats, where, over the
- * partition's tokens t and with x_t = scale * log2(e) * q.k_t,
+ * Split-KV workspace.  With partition_size > 0 the decode work is split and
+ * merged with a log-sum-exp reduction.  The 16-token tiles of all (sequence,
+ * KV head) pairs form one line that is cut into equal slices, one per worker
+ * (a single-wave workgroup; as many workers as fit on the device at once, at
+ * most 4096).  A slice is cut further at pair boundaries and at partition
+ * boundaries (every partition_size tokens of a pair), and each piece yields
+ * one record
+ *   float o[G][head_dim], m[G], l[G]; uint32 stamp      (G = heads per KV head)
+ * where, over the piece's tokens t and with x_t = scale * log2(e) * q.k_t,
  *   m = max_t x_t,  l = sum_t 2^(x_t - m),  o = sum_t 2^(x_t - m) v_t.
- * Record (s, g, p) starts at float offset
- *   ((s * num_kv_heads + g) * max_partitions + p) * R,
- * max_partitions = ceil(max_context_len / partition_size).  The workspace
- * must be 16-byte aligned.
- * pa_decode_workspace_bytes returns the byte size of that array (0 when
- * partition_size == 0, i.e. single pass, or when there is nothing to do).
+ * A piece that is a whole pair writes its output directly instead.  The
+ * workspace holds a small block of per-launch metadata and the records; it
+ * must be 16-byte aligned and at least pa_decode_workspace_bytes() long.
+ * Allocate it zero-filled once and reuse it: each launch stamps its records,
+ * so records left by earlier launches are ignored (zero is never a stamp).
+ * pa_decode_workspace_bytes returns 0 when partition_size == 0 (single pass,
+ * no workspace) or an argument is invalid.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len,
@@ -199,14 +202,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 
 /*
  * pa_decode_partials / pa_decode_merge -- the two phases pa_decode runs when
- * partition_size > 0, callable one by one (same arguments as pa_decode).
- * pa_decode_partials writes the record of every (s, g, p) with p <
- * ceil(L_s / partition_size) when that count is >= 2; sequences with a single
- * partition (or L_s == 0) get their final output written to out directly and
- * no record.  pa_decode_merge combines the records of each sequence with two
- * or more partitions, M = max_p m_p, w_p = 2^(m_p - M),
- * out = sum_p w_p o_p / sum_p w_p l_p, and leaves the other rows of out
- * untouched.
+ * partition_size > 0, callable one by one with the same arguments and
+ * workspace, partials first.  pa_decode_partials writes the records (and the
+ * outputs of pairs that are a single piece); pa_decode_merge combines each
+ * remaining pair's records, M = max_p m_p, w_p = 2^(m_p - M),
+ * out = sum_p w_p o_p / sum_p w_p l_p, and writes zeros for sequences of
+ * length 0.
  */
 int pa_decode_partials(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,

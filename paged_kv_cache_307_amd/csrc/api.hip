@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <tuple>
 #include <vector>
@@ -92,6 +93,14 @@ int64_t workspace_bytes_for(int32_t num_seqs, int32_t num_kv_heads, int32_t grou
                                         pa::record_floats(group, head_dim) * int64_t(sizeof(float));
 }
 
+// Stamp of a split-KV launch: records written by the launch carry it, so the
+// merge can tell them from records left in the workspace by earlier launches.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0x1234567u};
+  uint32_t e = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+  return e == 0 ? 1u : e;
+}
+
 int decode_workers(bool bf16, int head_dim, int block_size) {
   return bf16 ? pa::decode_workers_bf16_mfma(head_dim, block_size)
               : pa::decode_workers_simt(head_dim, false);
@@ -141,6 +150,7 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
     a.partition_size = partition_size;
     a.max_partitions = int32_t(parts);
     a.split = 1;
+    a.epoch = next_epoch();
   } else {
     if (int64_t(num_seqs) * num_kv_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
     a.partition_size = int32_t(std::max<int64_t>(16, (max_len + 15) / 16 * 16));

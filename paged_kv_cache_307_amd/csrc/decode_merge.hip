@@ -5,12 +5,12 @@
 // the piece's maximum of scale * log2(e) * q.k, l_p = sum of 2^(x - m_p),
 // o_p = sum of 2^(x - m_p) v), the exact softmax result is
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p l_p.
-// The pieces of a pair are found by walking the same cuts the workers made
-// (schedule.h).  Pairs written whole by one worker are left alone; pairs of
-// length 0 get zeros.
+// A pair's records lie in a short index range (schedule.h); records of this
+// launch carry its epoch stamp.  Pairs written whole by one worker are left
+// alone; pairs of length 0 get zeros.
 //
 // One 256-thread workgroup per (sequence, query head).  Thread t handles the
-// 16-byte dim chunk t % (D/4) of every (1024/D)-th piece, so each load is a
+// 16-byte dim chunk t % (D/4) of every (1024/D)-th record, so each load is a
 // coalesced float4; the partial sums meet in LDS.
 
 #include <math.h>
@@ -42,26 +42,10 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float4 v) {
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
-__device__ __forceinline__ float block_reduce(float x, float* sm, bool is_max) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float y = __shfl_xor(x, m);
-    x = is_max ? fmaxf(x, y) : x + y;
-  }
-  const int wave = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sm[wave] = x;
-  __syncthreads();
-  float r = sm[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) r = is_max ? fmaxf(r, sm[w]) : r + sm[w];
-  return r;
-}
-
 template <typename Elem, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
   constexpr int CH = D / 4;             // float4 chunks per head
-  constexpr int PG = kThreads / CH;     // piece groups
+  constexpr int PG = kThreads / CH;     // record groups
   const int sh = blockIdx.x;
   const int h = sh % a.num_heads;
   const int s = sh / a.num_heads;
@@ -69,56 +53,66 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
   const int kvh = h / G;
   const int hl = h % G;
   Elem* out = static_cast<Elem*>(a.out) + (int64_t(s) * a.num_heads + h) * D;
-  if (effective_len(a, s, B) == 0) {
+  PairRecords pr;
+  if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
     for (int i = threadIdx.x; i < D; i += kThreads) out[i] = from_f32<Elem>(0.f);
     return;
   }
-  const int npieces = for_each_piece(a, B, s, kvh, [](int64_t) {});
-  if (npieces <= 1) return;  // written whole by its worker
+  if (pr.whole) return;  // written whole by its worker
   const int64_t R = record_floats(G, D);
-  const float* recs = a.ws;
+  const float* base = a.ws + pr.first * R;
+  const int count = int(pr.last - pr.first + 1);
+  auto live = [&](const float* rec) { return __float_as_uint(rec[G * D + 2 * G]) == pr.epoch; };
 
-  __shared__ float sm_red[kThreads / 64];
-  __shared__ float4 sm_num[PG][CH];
-
-  float mloc = -INFINITY;
-  {
-    int q = 0;
-    for_each_piece(a, B, s, kvh, [&](int64_t idx) {
-      if (q % kThreads == int(threadIdx.x)) mloc = fmaxf(mloc, recs[idx * R + G * D + hl]);
-      ++q;
-    });
-  }
-  const float M = block_reduce(mloc, sm_red, true);
-  float dloc = 0.f;
+  // One pass: thread (pg, c) folds records pg, pg + PG, ... into a running
+  // (max, denominator, numerator chunk c), rescaling when the max grows.
   const int c = threadIdx.x % CH;
   const int pg = threadIdx.x / CH;
+  float m_t = -INFINITY, den_t = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  {
-    int q = 0;
-    for_each_piece(a, B, s, kvh, [&](int64_t idx) {
-      const float* rec = recs + idx * R;
-      if (q % kThreads == int(threadIdx.x)) dloc += exp2f(rec[G * D + hl] - M) * rec[G * D + G + hl];
-      if (q % PG == pg) {
-        const float w = exp2f(rec[G * D + hl] - M);
-        const float4 o = *reinterpret_cast<const float4*>(rec + hl * D + 4 * c);
-        num.x += w * o.x;
-        num.y += w * o.y;
-        num.z += w * o.z;
-        num.w += w * o.w;
-      }
-      ++q;
-    });
+  for (int q = pg; q < count; q += PG) {
+    const float* rec = base + q * R;
+    if (!live(rec)) continue;
+    const float m_q = rec[G * D + hl];
+    const float l_q = rec[G * D + G + hl];
+    const float4 o = *reinterpret_cast<const float4*>(rec + hl * D + 4 * c);
+    if (m_q > m_t) {
+      const float r = exp2f(m_t - m_q);  // 0 on the first record
+      den_t *= r;
+      num.x *= r; num.y *= r; num.z *= r; num.w *= r;
+      m_t = m_q;
+    }
+    const float w = exp2f(m_q - m_t);
+    den_t += w * l_q;
+    num.x += w * o.x;
+    num.y += w * o.y;
+    num.z += w * o.z;
+    num.w += w * o.w;
   }
-  const float den = block_reduce(dloc, sm_red, false);
+  __shared__ float sm_m[PG];
+  __shared__ float sm_den[PG];
+  __shared__ float4 sm_num[PG][CH];
+  if (c == 0) {
+    sm_m[pg] = m_t;
+    sm_den[pg] = den_t;
+  }
   sm_num[pg][c] = num;
   __syncthreads();
   if (threadIdx.x < CH) {
-    float4 t = sm_num[0][c];
+    float M = -INFINITY;
 #pragma unroll
-    for (int g = 1; g < PG; ++g) {
+    for (int g = 0; g < PG; ++g) M = fmaxf(M, sm_m[g]);
+    float den = 0.f;
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int g = 0; g < PG; ++g) {
+      // a group that saw no record has den == 0 (a record has l >= 1, or
+      // NaN when a broken block id poisoned it, which must propagate)
+      if (sm_den[g] == 0.f) continue;
+      const float w = exp2f(sm_m[g] - M);
+      den += w * sm_den[g];
       const float4 u = sm_num[g][c];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+      t.x += w * u.x; t.y += w * u.y; t.z += w * u.z; t.w += w * u.w;
     }
     const float inv = 1.0f / den;
     t.x *= inv; t.y *= inv; t.z *= inv; t.w *= inv;

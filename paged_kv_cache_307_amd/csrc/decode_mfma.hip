@@ -59,6 +59,7 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 64;  // one wave per worker
 constexpr int kTile = 16;
 constexpr float kRescaleThreshold = 8.0f;
+constexpr int kRing = 2;  // register tiles in the load ring
 
 template <int D>
 struct Tile {
@@ -261,27 +262,32 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                                                            pop, acc[c], 0, 0, 0);
     };
 
-    // Software pipeline over the piece's tiles: while tile k is consumed the
-    // loads of tile k+1 are in flight and the block ids of tile k+2 are
-    // being fetched.  The loads are issued unconditionally (past the last
-    // tile they repeat it, and the caches serve the repeat), so the wait
-    // before each tile covers exactly the loads issued before it.
+    // Software pipeline over the piece's tiles, a ring of kRing register
+    // tiles: while tile k is consumed, tiles k+1 .. k+kRing-1 are in flight
+    // and the block ids of the next tile to load are being fetched.  Every
+    // load is issued unconditionally (past the last tile the ring repeats
+    // the last tile, which the caches serve) and only the consumes are
+    // guarded, so the wait before each tile covers exactly the loads issued
+    // before it.
     {
-      Tile<D> r0, r1;
+      Tile<D> ring[kRing];
       const int last = ntile - 1;
-      TileIds id = fetch_ids<B>(row, t0_of(0), nblk);
-      load_tile<D, B>(r0, a, id, kvh, t0_of(0), lane, k_off, v_off);
-      id = fetch_ids<B>(row, t0_of(min(1, last)), nblk);
-      for (int k = 0; k < ntile; k += 2) {
-        load_tile<D, B>(r1, a, id, kvh, t0_of(min(k + 1, last)), lane, k_off, v_off);
-        id = fetch_ids<B>(row, t0_of(min(k + 2, last)), nblk);
-        __builtin_amdgcn_sched_barrier(0);  // keep the id fetch ahead of this tile's math
-        consume(r0, k);
-        if (k + 1 >= ntile) break;
-        load_tile<D, B>(r0, a, id, kvh, t0_of(min(k + 2, last)), lane, k_off, v_off);
-        id = fetch_ids<B>(row, t0_of(min(k + 3, last)), nblk);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(r1, k + 1);
+      TileIds id;
+#pragma unroll
+      for (int d = 0; d < kRing - 1; ++d) {
+        id = fetch_ids<B>(row, t0_of(min(d, last)), nblk);
+        load_tile<D, B>(ring[d], a, id, kvh, t0_of(min(d, last)), lane, k_off, v_off);
+      }
+      id = fetch_ids<B>(row, t0_of(min(kRing - 1, last)), nblk);
+      for (int k = 0; k < ntile; k += kRing) {
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+          const int kl = min(k + d + kRing - 1, last);
+          load_tile<D, B>(ring[(d + kRing - 1) % kRing], a, id, kvh, t0_of(kl), lane, k_off, v_off);
+          id = fetch_ids<B>(row, t0_of(min(k + d + kRing, last)), nblk);
+          __builtin_amdgcn_sched_barrier(0);  // keep the id fetch ahead of this tile's math
+          if (k + d < ntile) consume(ring[d], k + d);
+        }
       }
     }
 
@@ -305,6 +311,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
         if (grp == 0) {
           rec[G * D + col] = m_run;
           rec[G * D + G + col] = l_tot;
+          if (col == 0) rec[G * D + 2 * G] = __uint_as_float(a.epoch);
         }
       }
     }

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(64) void decode_simt_kernel(DecodeArgs a, int B) {
         if (lane == 0) {
           rec[G * D + h] = m_run[h];
           rec[G * D + G + h] = l_tot;
+          if (h == 0) rec[G * D + 2 * G] = __uint_as_float(a.epoch);
         }
       }
     }

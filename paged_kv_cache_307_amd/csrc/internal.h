@@ -21,6 +21,7 @@ struct DecodeArgs {
   float* ws;                  // split-KV records (see schedule.h), nullptr in single pass
   void* ws_meta;              // split-KV meta block: prefT, prefP, N
   int32_t workers;            // split-KV worker grid
+  uint32_t epoch;             // split-KV launch stamp (marks this launch's records)
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
@@ -36,10 +37,10 @@ struct DecodeArgs {
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// Floats in one split-KV record: o[G][D], then m[G], l[G], padded so every
-// record starts on a 16-byte boundary.
+// Floats in one split-KV record: o[G][D], m[G], l[G], the launch epoch
+// (uint32 bits), padded so every record starts on a 16-byte boundary.
 __host__ __device__ inline int64_t record_floats(int group, int head_dim) {
-  return int64_t(group) * head_dim + 4 * ((group + 1) / 2);
+  return int64_t(group) * head_dim + (2 * group + 1 + 3) / 4 * 4;
 }
 
 // Launch `kernel` and return hipLaunchKernel's own status (never a stale

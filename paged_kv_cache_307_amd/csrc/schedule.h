@@ -26,11 +26,11 @@ namespace pa {
 // Largest worker grid the workspace is sized for.
 constexpr int kMaxWorkers = 4096;
 
-// Workspace layout (bytes): int32 prefT[S], int32 prefP[S], int64 N (at
-// an 8-aligned offset), padding to 256, then the float records.
+// Workspace layout (bytes): int32 prefT[S], int32 prefP[S], int64 N and
+// uint32 epoch (at an 8-aligned offset), padding to 256, then the records.
 __host__ __device__ inline int64_t meta_bytes(int num_seqs) {
   const int64_t n_off = (int64_t(num_seqs) * 8 + 7) / 8 * 8;
-  return (n_off + 8 + 255) / 256 * 256;
+  return (n_off + 16 + 255) / 256 * 256;
 }
 __host__ __device__ inline int64_t max_records(int num_seqs, int num_kv_heads, int64_t max_parts) {
   return int64_t(num_seqs) * num_kv_heads * max_parts + kMaxWorkers;
@@ -118,7 +118,10 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
     ct += ps.tiles;
     cp += ps.parts;
   }
-  if (publish && lane == 0) *meta_n(a) = r.n;
+  if (publish && lane == 0) {
+    *meta_n(a) = r.n;
+    *reinterpret_cast<uint32_t*>(meta_n(a) + 1) = a.epoch;
+  }
   const unsigned long long owner = __ballot(found_s >= 0);
   const int src = owner ? int(__builtin_ctzll(owner)) : 0;
   r.seq = wave_uniform(__shfl(found_s, src));
@@ -164,36 +167,33 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, 
   }
 }
 
-// Calls fn(record_index) for every piece of pair (s, g) in line order and
-// returns the number of pieces.  Needs the meta block written by worker 0.
-template <typename Fn>
-__device__ __forceinline__ int for_each_piece(const DecodeArgs& a, int block_size, int s, int g,
-                                              Fn&& fn) {
+// Record indices of pair (s, g): every piece of the pair has an index in
+// [first, last]; indices in that range that belong to no piece (a worker cut
+// falling on a partition cut skips one) hold records of older launches,
+// whose epoch differs.  Needs the meta block written by worker 0.  Returns
+// false when the pair has no tiles.
+struct PairRecords {
+  int64_t first, last;
+  bool whole;      // one piece: its worker wrote the output directly
+  uint32_t epoch;  // stamp of the launch that wrote the meta block
+};
+
+__device__ __forceinline__ bool pair_records(const DecodeArgs& a, int block_size, int s, int g,
+                                             PairRecords* pr) {
   const PairShape ps = pair_shape(a, s, block_size);
-  if (ps.tiles == 0) return 0;
+  if (ps.tiles == 0) return false;
   const int32_t* meta = reinterpret_cast<const int32_t*>(a.ws_meta);
   const int64_t n = *meta_n(a);
   const int Hkv = a.num_kv_heads;
-  const int tpp = a.partition_size / 16;
   const int64_t base = int64_t(meta[s]) * Hkv + int64_t(g) * ps.tiles;
   const int64_t gp0 = int64_t(meta[a.num_seqs + s]) * Hkv + int64_t(g) * ps.parts;
-  const int64_t stop = base + ps.tiles;
-  int b = owner_of(n, a.workers, base);
-  int64_t cut = slice_start(n, a.workers, b + 1);
-  int64_t cur = base;
-  int count = 0;
-  while (cur < stop) {
-    while (cur >= cut) {
-      ++b;
-      cut = slice_start(n, a.workers, b + 1);
-    }
-    const int part = int((cur - base) / tpp);
-    const int64_t end = min(min(stop, cut), base + int64_t(part + 1) * tpp);
-    fn(gp0 + part + b);
-    ++count;
-    cur = end;
-  }
-  return count;
+  const int b_first = owner_of(n, a.workers, base);
+  const int b_last = owner_of(n, a.workers, base + ps.tiles - 1);
+  pr->first = gp0 + b_first;
+  pr->last = gp0 + ps.parts - 1 + b_last;
+  pr->whole = b_first == b_last && ps.parts == 1;
+  pr->epoch = *reinterpret_cast<const uint32_t*>(meta_n(a) + 1);
+  return true;
 }
 
 }  // namespace pa

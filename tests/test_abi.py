@@ -118,14 +118,14 @@ def test_write_and_copy_reject_before_launch(lib):
 
 
 def test_workspace_size_formula(lib):
-    # meta block (int32 prefT[S], prefP[S], int64 N, padded to 256 bytes), then
-    # S*Hkv*max(1, ceil(L/P)) + 4096 records of o[G][D], m[G], l[G] padded
-    # to a multiple of 4 floats
+    # meta block (int32 prefT[S], prefP[S], int64 N, uint32 epoch, padded to
+    # 256 bytes), then S*Hkv*max(1, ceil(L/P)) + 4096 records of o[G][D],
+    # m[G], l[G] and a stamp, padded to a multiple of 4 floats
     def expect(S, Hq, Hkv, D, L, P):
         G = Hq // Hkv
         parts = max(1, -(-L // P))
-        rec = G * D + 4 * ((G + 1) // 2)
-        meta = ((S * 8 + 7) // 8 * 8 + 8 + 255) // 256 * 256
+        rec = G * D + (2 * G + 1 + 3) // 4 * 4
+        meta = ((S * 8 + 7) // 8 * 8 + 16 + 255) // 256 * 256
         return meta + (S * Hkv * parts + 4096) * rec * 4
     for args in [(64, 32, 8, 128, 4096, 512), (8, 32, 8, 128, 131072, 512), (3, 5, 5, 64, 100, 16),
                  (256, 64, 8, 128, 8192, 512), (4, 32, 8, 128, 512, 512), (2, 4, 2, 64, 0, 16)]:
