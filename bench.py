@@ -4,10 +4,15 @@
 
 A step is the whole hot path for one layer of a decode batch: slot-mapped
 write of each sequence's new K/V row (pa_write_kv), then paged decode
-attention (pa_decode_partials + pa_decode_merge, i.e. pa_decode with 512-token
-partitions).  The default workload is the Llama-3-8B-shaped decode layer:
-64 sequences, 32 query / 8 KV heads, head_dim 128, bf16, B=16, context lengths
-uniform on [512, 4096], pool 1.25x the blocks needed, shuffled.
+attention with split-KV, i.e. pa_decode's two launches called one by one
+(pa_decode_partials, timed with HIP events as the dominant kernel, then
+pa_decode_merge).  The partition size defaults to one at least as long as the
+workload's longest context (so records only arise where a worker's slice
+cuts a pair); the long-context workload keeps its 512-token partitions.
+
+The default workload is the Llama-3-8B-shaped decode layer: 64 sequences,
+32 query / 8 KV heads, head_dim 128, bf16, B=16, context lengths uniform on
+[512, 4096], pool 1.25x the blocks needed, shuffled.
 
 Inputs are synthetic (seeded) and resident in HBM before timing starts.  To
 keep the 256 MB last-level cache from serving K/V across steps, the step
@@ -21,6 +26,7 @@ time, roofline of the dominant kernel from HIP events, CPU-oracle baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,19 +40,35 @@ HBM_PEAK_GBS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, then WRITE_SIZE) over this script's default run, each scaled by
+# what the same counter reads for pa_copy_blocks on a known byte count (run
+# with --copy-calibration): FETCH_SIZE x 1.99183, WRITE_SIZE x 1.0.  Summary
+# and commands: profiles/decode_partials_llama3_8b_decode_hbm_bytes.md.  The
+# figure holds only for the kernel sources it was measured with.
+KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache_307_amd/csrc/schedule.h",
+                  "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
+                  "paged_kv_cache_307_amd/csrc/api.hip"]
+MEASURED_TRAFFIC = {
+    ("llama3_8b_decode", 4096): {"bytes": 544028091, "fetch_bytes": 541389870, "write_bytes": 2638221,
+                                 "sources_sha256": "e3c09214ac09da9b0f847ec8b7ae90f33e699a76e2abb4f0f019190a092ed2a9"},
+}
+
 
 def make_workload(name):
+    """(workload, default partition size)."""
     import workloads as W
     table = {
-        "llama3_8b_decode": W.llama3_8b_decode,
-        "long_context": W.long_context,
-        "shared_prefix_steady": lambda: W.shared_prefix("steady"),
-        "shared_prefix_fork": lambda: W.shared_prefix("fork"),
-        "mixed_lengths_B8": lambda: W.mixed_lengths(8),
-        "mixed_lengths_B16": lambda: W.mixed_lengths(16),
-        "mixed_lengths_B32": lambda: W.mixed_lengths(32),
+        "llama3_8b_decode": (W.llama3_8b_decode, 4096),
+        "long_context": (W.long_context, 512),
+        "shared_prefix_steady": (lambda: W.shared_prefix("steady"), 4096),
+        "shared_prefix_fork": (lambda: W.shared_prefix("fork"), 4096),
+        "mixed_lengths_B8": (lambda: W.mixed_lengths(8), 8192),
+        "mixed_lengths_B16": (lambda: W.mixed_lengths(16), 8192),
+        "mixed_lengths_B32": (lambda: W.mixed_lengths(32), 8192),
     }
-    return table[name]()
+    make, partition = table[name]
+    return make(), partition
 
 
 def algorithmic_bytes(w):
@@ -59,6 +81,23 @@ def algorithmic_bytes(w):
     table = int(sum(-(-int(x) // w.block_size) for x in L)) * 4
     return {"kv": kv, "q": q, "out": q, "table": table, "context_lens": 4 * w.num_seqs,
             "write": w.num_seqs * w.num_kv_heads * w.head_dim * e * 2 * 2 + 8 * w.num_seqs}
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, partition):
+    """Counter-derived HBM bytes per launch, or None when there is no
+    measurement for this workload or the kernel changed since it was taken."""
+    rec = MEASURED_TRAFFIC.get((workload, partition))
+    if rec is None or rec["sources_sha256"] != kernel_sources_sha256():
+        return None
+    return rec["bytes"]
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -118,7 +157,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama3_8b_decode")
-    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-KV partition size (default: per workload)")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -131,7 +171,7 @@ def main():
         copy_calibration()
         return
 
-    w = make_workload(args.workload)
+    w, default_partition = make_workload(args.workload)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     import torch
@@ -148,7 +188,8 @@ def main():
         return torch.from_numpy(x).to(dev)
 
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    B, P = w.block_size, args.partition
+    B = w.block_size
+    P = default_partition if args.partition is None else args.partition
     hist_bt, bt, cl = t(w.hist_block_tables), t(w.block_tables), t(w.context_lens)
     k0, v0 = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, B, w.head_dim, dt, dev,
                                fill=float("nan"))
@@ -221,11 +262,11 @@ def main():
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
         "roofline": {
-            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B}> (pa_decode_partials)",
+            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true> (pa_decode_partials)",
             "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(part_avg_ms * 1e3, 3), "bytes_per_launch": part_bytes,
-            "traffic": None,
+            "traffic": measured_traffic(w.name, P),
         },
         "cpu_baseline": cpu,
     }

@@ -187,7 +187,8 @@ def alloc_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len
                     device="cuda"):
     n = decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                                partition_size)
-    return torch.empty(max(n, 16) // 4 + 4, dtype=torch.float32, device=device)
+    # zero-filled once; launches stamp what they write, so it can be reused
+    return torch.zeros(max(n, 16) // 4 + 4, dtype=torch.float32, device=device)
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len):

@@ -16,6 +16,8 @@
 
 namespace pa {
 
+constexpr int kWorkersPerCu = 3;
+
 int resident_workers(const void* kernel, int block_threads) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -31,7 +33,10 @@ int resident_workers(const void* kernel, int block_threads) {
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess)
     return 0;
-  const int workers = std::min(kMaxWorkers, std::max(1, cus * per_cu));
+  // Three single-wave workers per compute unit: enough loads in flight to
+  // keep HBM busy, and the fewer the workers, the fewer the piece starts
+  // (each costs dependent memory round trips) per byte streamed.
+  const int workers = std::min(kMaxWorkers, std::max(1, cus * std::min(per_cu, kWorkersPerCu)));
   std::lock_guard<std::mutex> lock(mu);
   cache.emplace_back(kernel, dev, workers);
   return workers;

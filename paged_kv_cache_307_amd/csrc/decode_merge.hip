@@ -62,32 +62,45 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
   const int64_t R = record_floats(G, D);
   const float* base = a.ws + pr.first * R;
   const int count = int(pr.last - pr.first + 1);
-  auto live = [&](const float* rec) { return __float_as_uint(rec[G * D + 2 * G]) == pr.epoch; };
 
   // One pass: thread (pg, c) folds records pg, pg + PG, ... into a running
   // (max, denominator, numerator chunk c), rescaling when the max grows.
+  // The loads of kUnroll records are issued together and unconditionally
+  // (a stamp from another launch only drops the record afterwards), so a
+  // pair costs one round trip to memory per kUnroll records per thread.
+  constexpr int kUnroll = 2;
   const int c = threadIdx.x % CH;
   const int pg = threadIdx.x / CH;
   float m_t = -INFINITY, den_t = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q = pg; q < count; q += PG) {
-    const float* rec = base + q * R;
-    if (!live(rec)) continue;
-    const float m_q = rec[G * D + hl];
-    const float l_q = rec[G * D + G + hl];
-    const float4 o = *reinterpret_cast<const float4*>(rec + hl * D + 4 * c);
-    if (m_q > m_t) {
-      const float r = exp2f(m_t - m_q);  // 0 on the first record
-      den_t *= r;
-      num.x *= r; num.y *= r; num.z *= r; num.w *= r;
-      m_t = m_q;
+  for (int q0 = pg; q0 < count; q0 += PG * kUnroll) {
+    uint32_t st[kUnroll];
+    float mq[kUnroll], lq[kUnroll];
+    float4 oq[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float* rec = base + int64_t(min(q0 + u * PG, count - 1)) * R;
+      st[u] = __float_as_uint(rec[G * D + 2 * G]);
+      mq[u] = rec[G * D + hl];
+      lq[u] = rec[G * D + G + hl];
+      oq[u] = *reinterpret_cast<const float4*>(rec + hl * D + 4 * c);
     }
-    const float w = exp2f(m_q - m_t);
-    den_t += w * l_q;
-    num.x += w * o.x;
-    num.y += w * o.y;
-    num.z += w * o.z;
-    num.w += w * o.w;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (q0 + u * PG >= count || st[u] != pr.epoch) continue;
+      if (mq[u] > m_t) {
+        const float r = exp2f(m_t - mq[u]);  // 0 on the first record
+        den_t *= r;
+        num.x *= r; num.y *= r; num.z *= r; num.w *= r;
+        m_t = mq[u];
+      }
+      const float w = exp2f(mq[u] - m_t);
+      den_t += w * lq[u];
+      num.x += w * oq[u].x;
+      num.y += w * oq[u].y;
+      num.z += w * oq[u].z;
+      num.w += w * oq[u].w;
+    }
   }
   __shared__ float sm_m[PG];
   __shared__ float sm_den[PG];

@@ -36,9 +36,11 @@
 // updated running maximum: the accumulator is rescaled only when a tile's
 // maximum exceeds the maximum in use by more than 8 (a factor 256), which
 // keeps every weight <= 2^8 and is exact because the final division uses the
-// same maximum.  The block-table entry of a tile is wave-uniform and lives in
-// a scalar register; K/V addresses are a scalar 64-bit tile base plus a
-// per-lane 32-bit offset, so no vector ALU is spent on address arithmetic.
+// same maximum.  A piece's block-table entries are staged 64 at a time in a
+// vector register (one load per window, the next window loaded a window
+// ahead); a tile's entry is read from it into a scalar register.  K/V
+// addresses are a scalar 64-bit tile base plus a per-lane 32-bit offset, so
+// no vector ALU is spent on address arithmetic.
 // The next tile's loads are issued before the current tile is consumed.
 
 #include <math.h>
@@ -75,13 +77,29 @@ struct TileIds {
   int pb1;
 };
 
+// Block-table window: lane i holds the table entry of logical block b0 + i
+// (clamped to the sequence's last block, so every read stays in its row).
+// One vector load fetches the ids of up to 64 blocks; tiles then take their
+// ids from it with a lane read, off the memory path.
+__device__ __forceinline__ int load_window(const int32_t* row, int b0, int nblk, int lane) {
+  return row[min(b0 + lane, nblk - 1)];
+}
+
+// Tiles one window serves: their blocks must fit in 64 entries (with B = 32
+// a tile run may start in the middle of a block, costing one entry).
 template <int B>
-__device__ __forceinline__ TileIds fetch_ids(const int32_t* row, int t0, int nblk) {
+constexpr int window_tiles() {
+  return B < kTile ? 64 * B / kTile : (B == kTile ? 64 : 63 * B / kTile);
+}
+
+// Ids of the tile starting at token t0 from the window based at block wb.
+template <int B>
+__device__ __forceinline__ TileIds window_ids(int win, int wb, int t0, int nblk) {
   const int lb = t0 / B;
   TileIds id;
-  id.pb0 = load_ro(row, lb);
+  id.pb0 = __builtin_amdgcn_readlane(win, lb - wb);
   if constexpr (B < kTile) {
-    id.pb1 = (lb + 1 < nblk) ? load_ro(row, lb + 1) : id.pb0;
+    id.pb1 = (lb + 1 < nblk) ? __builtin_amdgcn_readlane(win, lb + 1 - wb) : id.pb0;
   } else {
     id.pb1 = id.pb0;
   }
@@ -263,31 +281,41 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     };
 
     // Software pipeline over the piece's tiles, a ring of kRing register
-    // tiles: while tile k is consumed, tiles k+1 .. k+kRing-1 are in flight
-    // and the block ids of the next tile to load are being fetched.  Every
-    // load is issued unconditionally (past the last tile the ring repeats
-    // the last tile, which the caches serve) and only the consumes are
-    // guarded, so the wait before each tile covers exactly the loads issued
-    // before it.
+    // tiles: while tile k is consumed, tiles k+1 .. k+kRing-1 are in flight.
+    // Every load is issued unconditionally (past the last tile the ring
+    // repeats the last tile, which the caches serve) and only the consumes
+    // are guarded, so the wait before each tile covers exactly the loads
+    // issued before it.  Block ids come from a table window; the window of
+    // the next run of tiles is loaded when the current run starts.
     {
+      constexpr int kWin = window_tiles<B>();
       Tile<D> ring[kRing];
-      const int last = ntile - 1;
-      TileIds id;
+      int win = load_window(row, t_begin / B, nblk, lane);
+      for (int k0 = 0; k0 < ntile; k0 += kWin) {
+        const int k1 = min(ntile, k0 + kWin);
+        const int wb = t0_of(k0) / B;
+        const int last = k1 - 1;
+        TileIds id;
 #pragma unroll
-      for (int d = 0; d < kRing - 1; ++d) {
-        id = fetch_ids<B>(row, t0_of(min(d, last)), nblk);
-        load_tile<D, B>(ring[d], a, id, kvh, t0_of(min(d, last)), lane, k_off, v_off);
-      }
-      id = fetch_ids<B>(row, t0_of(min(kRing - 1, last)), nblk);
-      for (int k = 0; k < ntile; k += kRing) {
-#pragma unroll
-        for (int d = 0; d < kRing; ++d) {
-          const int kl = min(k + d + kRing - 1, last);
-          load_tile<D, B>(ring[(d + kRing - 1) % kRing], a, id, kvh, t0_of(kl), lane, k_off, v_off);
-          id = fetch_ids<B>(row, t0_of(min(k + d + kRing, last)), nblk);
-          __builtin_amdgcn_sched_barrier(0);  // keep the id fetch ahead of this tile's math
-          if (k + d < ntile) consume(ring[d], k + d);
+        for (int d = 0; d < kRing - 1; ++d) {
+          const int kd = min(k0 + d, last);
+          id = window_ids<B>(win, wb, t0_of(kd), nblk);
+          load_tile<D, B>(ring[d], a, id, kvh, t0_of(kd), lane, k_off, v_off);
         }
+        id = window_ids<B>(win, wb, t0_of(min(k0 + kRing - 1, last)), nblk);
+        int nxt = win;  // issued after this window's first reads, so they do not wait for it
+        if (k1 < ntile) nxt = load_window(row, t0_of(k1) / B, nblk, lane);
+        for (int k = k0; k < k1; k += kRing) {
+#pragma unroll
+          for (int d = 0; d < kRing; ++d) {
+            const int kl = min(k + d + kRing - 1, last);
+            load_tile<D, B>(ring[(d + kRing - 1) % kRing], a, id, kvh, t0_of(kl), lane, k_off,
+                            v_off);
+            id = window_ids<B>(win, wb, t0_of(min(k + d + kRing, last)), nblk);
+            if (k + d < k1) consume(ring[d], k + d);
+          }
+        }
+        win = nxt;
       }
     }
 

@@ -75,8 +75,9 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs
 hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_size,
                                    hipStream_t stream);
 // Number of split-KV workers a decode kernel should use on the current
-// device: resident workgroups per compute unit x compute units, capped at
-// the workspace's worker bound.  0 on failure.  Cached per kernel and device.
+// device: compute units x min(resident workgroups per compute unit, 3),
+// capped at the workspace's worker bound.  0 on failure.  Cached per kernel
+// and device.
 int resident_workers(const void* kernel, int block_threads);
 int decode_workers_bf16_mfma(int head_dim, int block_size);
 int decode_workers_simt(int head_dim, bool bf16);
