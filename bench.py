@@ -2,11 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is the whole hot path for one layer of a decode batch: slot-mapped
-write of each sequence's new K/V row (pa_write_kv), then paged decode
-attention with split-KV, i.e. pa_decode's two launches called one by one
-(pa_decode_partials, timed with HIP events as the dominant kernel, then
-pa_decode_merge).  The partition size defaults to one at least as long as the
+A step is the whole hot path for one layer of a decode batch: the write of
+each sequence's new K/V row at its slot, then paged decode attention with
+split-KV.  By default the step is pa_append_decode's two launches called one
+by one: pa_append_decode_partials (the decode workers also store the step's
+rows; timed with HIP events as the dominant kernel), then pa_decode_merge.
+With --separate-write the rows go through pa_write_kv first and the decode
+is pa_decode_partials + pa_decode_merge.  The partition size defaults to one at least as long as the
 workload's longest context (so records only arise where a worker's slice
 cuts a pair); the long-context workload keeps its 512-token partitions.
 
@@ -50,7 +52,7 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
                   "paged_kv_cache_307_amd/csrc/api.hip"]
 MEASURED_TRAFFIC = {
-    ("llama3_8b_decode", 4096): {"bytes": 544028091, "fetch_bytes": 541389870, "write_bytes": 2638221,
+    ("llama3_8b_decode", 4096, False): {"bytes": 544028091, "fetch_bytes": 541389870, "write_bytes": 2638221,
                                  "sources_sha256": "e3c09214ac09da9b0f847ec8b7ae90f33e699a76e2abb4f0f019190a092ed2a9"},
 }
 
@@ -72,15 +74,16 @@ def make_workload(name):
 
 
 def algorithmic_bytes(w):
-    """Bytes the decode must move at minimum: K and V of live tokens, q,
-    out, the table entries in use and the context lengths."""
+    """Bytes one step must move at minimum: K and V of the live tokens read
+    once (the step's own row included), q, out, the table entries in use, the
+    context lengths, and the step's K/V rows stored to the cache."""
     e = w.elem_bytes
     L = w.context_lens.astype(np.int64)
     kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * e
     q = w.num_seqs * w.num_heads * w.head_dim * e
     table = int(sum(-(-int(x) // w.block_size) for x in L)) * 4
     return {"kv": kv, "q": q, "out": q, "table": table, "context_lens": 4 * w.num_seqs,
-            "write": w.num_seqs * w.num_kv_heads * w.head_dim * e * 2 * 2 + 8 * w.num_seqs}
+            "write": int((L > 0).sum()) * w.num_kv_heads * w.head_dim * e * 2}
 
 
 def kernel_sources_sha256():
@@ -91,10 +94,10 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload, partition):
+def measured_traffic(workload, partition, append):
     """Counter-derived HBM bytes per launch, or None when there is no
-    measurement for this workload or the kernel changed since it was taken."""
-    rec = MEASURED_TRAFFIC.get((workload, partition))
+    measurement for this workload and step or the kernel changed since."""
+    rec = MEASURED_TRAFFIC.get((workload, partition, append))
     if rec is None or rec["sources_sha256"] != kernel_sources_sha256():
         return None
     return rec["bytes"]
@@ -161,6 +164,8 @@ def main():
                     help="split-KV partition size (default: per workload)")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the step's rows with pa_write_kv, then pa_decode_partials")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks on a known byte count (profiler calibration)")
     args = ap.parse_args()
@@ -207,10 +212,14 @@ def main():
 
     def step(i, ev=None):
         k, v = layers[i % len(layers)]
-        pa.write_kv(k, v, new_k, new_v, new_slots)
+        if args.separate_write:
+            pa.write_kv(k, v, new_k, new_v, new_slots)
         if ev is not None:
             ev[0].record()
-        pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out)
+        if args.separate_write:
+            pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out)
+        else:
+            pa.append_decode_partials(q, new_k, new_v, k, v, bt, cl, mcl, w.scale, P, ws, out)
         if ev is not None:
             ev[1].record()
         pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
@@ -234,7 +243,11 @@ def main():
     step_bytes = sum(ab.values())
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     part_avg_ms = float(np.mean(part_ms))
+    # the timed kernel: reads K/V, q, table entries and lengths; in the
+    # appending step it also stores the rows (the merge writes most of out)
     part_bytes = ab["kv"] + ab["q"] + ab["table"] + ab["context_lens"]
+    if not args.separate_write:
+        part_bytes += ab["write"]
     part_gbs = part_bytes / (part_avg_ms * 1e-3) / 1e9
     L = w.context_lens
     rec = {
@@ -256,17 +269,19 @@ def main():
             "context_len_min": int(L.min()), "context_len_max": int(L.max()),
             "context_len_mean": round(float(L.mean()), 1), "num_blocks": w.num_blocks,
             "partition_size": P, "layers_rotated": args.layers,
-            "step": "pa_write_kv + pa_decode_partials + pa_decode_merge",
+            "step": ("pa_write_kv + pa_decode_partials + pa_decode_merge" if args.separate_write
+                     else "pa_append_decode_partials + pa_decode_merge"),
         },
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
         "roofline": {
-            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true> (pa_decode_partials)",
+            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true> (" +
+                      ("pa_decode_partials" if args.separate_write else "pa_append_decode_partials") + ")",
             "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(part_avg_ms * 1e3, 3), "bytes_per_launch": part_bytes,
-            "traffic": measured_traffic(w.name, P),
+            "traffic": measured_traffic(w.name, P, not args.separate_write),
         },
         "cpu_baseline": cpu,
     }

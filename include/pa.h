@@ -221,6 +221,45 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
                     int32_t block_size, int32_t max_context_len, int32_t partition_size,
                     const void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
 
+/*
+ * pa_append_decode / pa_append_decode_partials -- a decode step that also
+ * stores the step's own K/V row.
+ * [P3 对 ModelRunner 的影响: the current token's K/V go to its slot and the
+ *  kernel attends over the context through the block table; P2 BlockTable
+ *  walkthrough: slot = block_table[s][pos // B] * B + pos % B.]
+ *
+ *   key, value        in      [num_seqs][num_kv_heads][head_dim], 16-byte
+ *                             aligned: row s is the K/V of sequence s's
+ *                             token at position L_s - 1
+ *   k_cache, v_cache  in/out  pools in the layout above
+ *   every other argument as pa_decode / pa_decode_partials
+ *
+ * The result equals pa_write_kv of row s at the slot of position L_s - 1
+ * (L_s the clamped context length; nothing is written for L_s == 0 or a
+ * table entry outside [0, num_blocks)) followed by pa_decode (respectively
+ * pa_decode_partials, to be followed by pa_decode_merge).  For bf16 the
+ * write is part of the decode launch: the worker that owns the last tile of
+ * each (sequence, KV head) stores that head's row and uses it in its tile,
+ * so no other launch or wave touches the slot.  For fp32 a write launch
+ * precedes the decode.  Errors as pa_decode, plus PA_ERR_INVALID_ARG for a
+ * missing or misaligned key/value (with num_seqs > 0).
+ */
+int pa_append_decode(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                     void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, float scale, int32_t partition_size,
+                     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+
+int pa_append_decode_partials(void* out, const void* q, const void* key, const void* value,
+                              void* k_cache, void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, int32_t dtype,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

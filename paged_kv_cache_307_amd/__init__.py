@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     PA_DTYPE_F32,
     PagedAttentionError,
     alloc_workspace,
+    append_decode,
+    append_decode_partials,
     copy_blocks,
     decode,
     decode_merge,

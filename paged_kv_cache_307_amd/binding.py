@@ -24,6 +24,7 @@ _DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
 EXPORTED = (
     "pa_status_string", "pa_slot_mapping", "pa_write_kv", "pa_copy_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partials", "pa_decode_merge",
+    "pa_append_decode", "pa_append_decode_partials",
 )
 
 
@@ -55,6 +56,11 @@ def load_library():
         "pa_decode_partials": (ctypes.c_int,
                                [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, P]),
         "pa_decode_merge": (ctypes.c_int, [P, P, I, I, I, I, I, I, I, I, P, Z, I, P]),
+        "pa_append_decode": (ctypes.c_int,
+                             [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, P]),
+        "pa_append_decode_partials": (ctypes.c_int,
+                                      [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z,
+                                       I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -247,4 +253,45 @@ def decode_merge(out, context_lens, num_kv_heads, block_size, max_blocks_per_seq
         int(block_size), int(max_context_len), int(partition_size), _ptr(workspace), ws_bytes,
         _dtype_code(out), _stream(stream))
     _check(st, "pa_decode_merge")
+    return out
+
+
+def _append_args(key, value, q, hkv, d):
+    _cuda_contig("key", key, q.dtype)
+    _cuda_contig("value", value, q.dtype)
+    s = q.shape[0]
+    _need(tuple(key.shape) == (s, hkv, d) and tuple(value.shape) == (s, hkv, d),
+          "key/value must be [S, Hkv, D]")
+
+
+def append_decode(q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len,
+                  scale, partition_size=0, workspace=None, out=None, stream=None):
+    """Store each sequence's new K/V row at position L - 1, then decode."""
+    if out is None:
+        out = torch.empty_like(q)
+    dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
+    s, hq, hkv, d, b, nb, mb, mcl = dims
+    _append_args(key, value, q, hkv, d)
+    if partition_size and workspace is None:
+        workspace = alloc_workspace(s, hq, hkv, d, mcl, partition_size, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().pa_append_decode(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, b, nb, mb, mcl, float(scale),
+        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream))
+    _check(st, "pa_append_decode")
+    return out
+
+
+def append_decode_partials(q, key, value, k_cache, v_cache, block_tables, context_lens,
+                           max_context_len, scale, partition_size, workspace, out, stream=None):
+    dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
+    s, hq, hkv, d, b, nb, mb, mcl = dims
+    _append_args(key, value, q, hkv, d)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().pa_append_decode_partials(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, b, nb, mb, mcl, float(scale),
+        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream))
+    _check(st, "pa_append_decode_partials")
     return out

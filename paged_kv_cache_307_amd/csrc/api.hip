@@ -182,9 +182,26 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
   return PA_OK;
 }
 
+// The decode launch of a plan.  With an appended row (plan.args.new_k set)
+// the matrix-core kernel writes and uses the row itself; the fp32 kernel
+// runs after a separate append launch.
 hipError_t launch_partials(const DecodePlan& plan, hipStream_t stream) {
   if (plan.bf16) return pa::launch_decode_bf16_mfma(plan.args, plan.head_dim, plan.block_size, stream);
-  return pa::launch_decode_simt(plan.args, plan.head_dim, plan.block_size, false, stream);
+  DecodeArgs a = plan.args;
+  if (a.new_k) {
+    const hipError_t e = pa::launch_append_kv(a, plan.head_dim, plan.block_size, 4, stream);
+    if (e != hipSuccess) return e;
+    a.new_k = a.new_v = nullptr;
+  }
+  return pa::launch_decode_simt(a, plan.head_dim, plan.block_size, false, stream);
+}
+
+// Checks of the appended rows (after plan_decode accepted the rest).
+int check_append(const void* key, const void* value, int32_t num_seqs) {
+  if (num_seqs == 0) return PA_OK;
+  if (!key || !value) return PA_ERR_INVALID_ARG;
+  if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID_ARG;
+  return PA_OK;
 }
 
 }  // namespace
@@ -329,6 +346,50 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                              max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                              workspace_bytes, dtype);
   if (st != PA_OK || plan.args.num_seqs == 0) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_partials(plan, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (plan.split) e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);
+  return status_of(e);
+}
+
+int pa_append_decode_partials(void* out, const void* q, const void* key, const void* value,
+                              void* k_cache, void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, int32_t dtype,
+                              void* stream) {
+  DecodePlan plan;
+  int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, dtype);
+  if (st != PA_OK) return st;
+  st = check_append(key, value, num_seqs);
+  if (st != PA_OK || plan.args.num_seqs == 0) return st;
+  plan.args.new_k = key;
+  plan.args.new_v = value;
+  return status_of(launch_partials(plan, static_cast<hipStream_t>(stream)));
+}
+
+int pa_append_decode(void* out, const void* q, const void* key, const void* value, void* k_cache,
+                     void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                     int32_t max_context_len, float scale, int32_t partition_size,
+                     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+  DecodePlan plan;
+  int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, dtype);
+  if (st != PA_OK) return st;
+  st = check_append(key, value, num_seqs);
+  if (st != PA_OK || plan.args.num_seqs == 0) return st;
+  plan.args.new_k = key;
+  plan.args.new_v = value;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_partials(plan, s);
   if (e != hipSuccess) return PA_ERR_HIP;

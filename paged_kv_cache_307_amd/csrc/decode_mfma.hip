@@ -179,9 +179,100 @@ __device__ __forceinline__ float colsum4(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+// Appending decode: the step's own K/V row (token L - 1) of a (sequence, KV
+// head) is read from the caller's key/value arrays and held spread over the
+// wave, E = kRowElems dims per lane (lane m holds dims [mE, mE + E)).
+template <int D>
+struct NewRow {
+  static constexpr int kElems = D >= 256 ? 4 : 2;  // dims per lane
+  static constexpr int kDwords = kElems / 2;
+  static constexpr int kLanes = D / kElems;        // lanes holding data
+  uint32_t k[kDwords];
+  uint32_t v[kDwords];
+};
+
+template <int D>
+__device__ __forceinline__ NewRow<D> load_new_row(const DecodeArgs& a, int s, int kvh, int lane) {
+  NewRow<D> nr;
+  const int64_t row = (int64_t(s) * a.num_kv_heads + kvh) * (D / 2);  // in dwords
+  const int m = min(lane, NewRow<D>::kLanes - 1);
+  const uint32_t* kr = static_cast<const uint32_t*>(a.new_k) + row + m * NewRow<D>::kDwords;
+  const uint32_t* vr = static_cast<const uint32_t*>(a.new_v) + row + m * NewRow<D>::kDwords;
+#pragma unroll
+  for (int i = 0; i < NewRow<D>::kDwords; ++i) {
+    nr.k[i] = kr[i];
+    nr.v[i] = vr[i];
+  }
+  return nr;
+}
+
+// Stage the new row in the wave's LDS buffer (K row, then V row).
+template <int D>
+__device__ __forceinline__ void stage_new_row(const NewRow<D>& nr, uint32_t* lds, int lane) {
+  if (lane < NewRow<D>::kLanes) {
+#pragma unroll
+    for (int i = 0; i < NewRow<D>::kDwords; ++i) {
+      lds[lane * NewRow<D>::kDwords + i] = nr.k[i];
+      lds[D / 2 + lane * NewRow<D>::kDwords + i] = nr.v[i];
+    }
+  }
+  __syncthreads();  // one wave: orders the LDS writes before later reads
+}
+
+// Put the staged row into the operand registers of the tile holding token
+// rt (0..15 within the tile): the K operand lanes of row rt read their
+// 16-byte chunks straight into place, and the V operand lanes holding token
+// rt insert one value per dim chunk.
+template <int D>
+__device__ __forceinline__ void put_new_row(Tile<D>& r, const uint32_t* lds, int rt, int col,
+                                            int grp) {
+  const uint16_t* kl = reinterpret_cast<const uint16_t*>(lds);
+  const uint16_t* vl = kl + D;
+  if (col == rt) {
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) r.k[j] = *reinterpret_cast<const uint4*>(kl + 32 * j + 8 * grp);
+  }
+  if (grp == rt / 4) {
+    const int half = 16 * (rt % 2);
+    const uint32_t keep = ~(0xFFFFu << half);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const uint32_t val = vl[16 * c + col];
+      if (rt % 4 < 2)
+        r.v[c].x = (r.v[c].x & keep) | (val << half);
+      else
+        r.v[c].y = (r.v[c].y & keep) | (val << half);
+    }
+  }
+}
+
+// Store the new row at position p of the pair, block pb (a valid id).
+template <int D, int B>
+__device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewRow<D>& nr, int pb,
+                                              int kvh, int p, int lane) {
+  constexpr int E = NewRow<D>::kElems;
+  if (lane >= NewRow<D>::kLanes) return;
+  const int64_t tile = int64_t(pb) * a.num_kv_heads + kvh;
+  // the pools are writable when a row is appended (the API takes them non-const)
+  uint16_t* kd = static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + (tile * B + p % B) * D +
+                 lane * E;
+  uint16_t* vd = static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) +
+                 (tile * D + lane * E) * B + p % B;
+  if constexpr (E == 2) {
+    *reinterpret_cast<uint32_t*>(kd) = nr.k[0];
+  } else {
+    *reinterpret_cast<uint2*>(kd) = make_uint2(nr.k[0], nr.k[1]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t dw = nr.v[e / 2];
+    vd[e * B] = uint16_t((e % 2) ? dw >> 16 : dw & 0xFFFFu);
+  }
+}
+
 template <int D, int B, bool kSplit>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : (B >= kTile ? 3 : 2))))
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2)))
 void decode_bf16_mfma_kernel(DecodeArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int DCH = D / 16;
@@ -190,6 +281,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   const int col = lane & 15;
   const int grp = lane >> 4;
   uint16_t* out = static_cast<uint16_t*>(a.out);
+  __shared__ uint32_t new_row_lds[D];  // appending decode: the new K row, then the V row
 
   // Per-lane byte offsets inside a tile.
   const uint32_t k_off = uint32_t(col) * D * 2 + uint32_t(grp) * 16;
@@ -210,6 +302,16 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     const int t_end = min(L, (tin + ntile) * kTile);
     const int nblk = (L + B - 1) / B;
     const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
+
+    // Appending decode: the piece holding the pair's last tile writes the
+    // step's row (token L - 1) to its slot and uses it in that tile.
+    const bool append = a.new_k != nullptr && tin + ntile == (L + kTile - 1) / kTile;
+    NewRow<D> nr{};
+    int pb_new = 0;
+    if (append) {  // issued first: its wait below overlaps the table window's
+      nr = load_new_row<D>(a, s, kvh, lane);
+      pb_new = load_ro(row, (L - 1) / B);
+    }
 
     // Q^T operand: column col = query head kvh*G + col (zero beyond G).
     bf16x8_t qop[KSTEPS];
@@ -291,6 +393,13 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       constexpr int kWin = window_tiles<B>();
       Tile<D> ring[kRing];
       int win = load_window(row, t_begin / B, nblk, lane);
+      if (append) {
+        // the row goes to LDS for the last tile, and to its slot in the cache
+        // (only this wave reads that slot in this launch)
+        stage_new_row<D>(nr, new_row_lds, lane);
+        if (unsigned(pb_new) < unsigned(a.num_blocks))
+          store_new_row<D, B>(a, nr, pb_new, kvh, L - 1, lane);
+      }
       for (int k0 = 0; k0 < ntile; k0 += kWin) {
         const int k1 = min(ntile, k0 + kWin);
         const int wb = t0_of(k0) / B;
@@ -312,7 +421,11 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
             load_tile<D, B>(ring[(d + kRing - 1) % kRing], a, id, kvh, t0_of(kl), lane, k_off,
                             v_off);
             id = window_ids<B>(win, wb, t0_of(min(k + d + kRing, last)), nblk);
-            if (k + d < k1) consume(ring[d], k + d);
+            if (k + d < k1) {
+              if (append && k + d == ntile - 1)
+                put_new_row<D>(ring[d], new_row_lds, t_end - 1 - t0_of(k + d), col, grp);
+              consume(ring[d], k + d);
+            }
           }
         }
         win = nxt;

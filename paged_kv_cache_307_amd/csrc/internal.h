@@ -18,6 +18,8 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const void* new_k;          // append: K row [S][Hkv][D] of each sequence's token L - 1, or null
+  const void* new_v;          // append: V row, same shape
   float* ws;                  // split-KV records (see schedule.h), nullptr in single pass
   void* ws_meta;              // split-KV meta block: prefT, prefP, N
   int32_t workers;            // split-KV worker grid
@@ -66,6 +68,10 @@ hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_tables, cons
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const void* value,
                            const int64_t* slots, int num_tokens, int num_kv_heads, int head_dim,
                            int block_size, int num_blocks, int elem_bytes, hipStream_t stream);
+// Write key/value row s at position context_lens[s] - 1 (clamped as in the
+// decode) of sequence s, through its block table.
+hipError_t launch_append_kv(const DecodeArgs& a, int head_dim, int block_size, int elem_bytes,
+                            hipStream_t stream);
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int num_pairs,
                               int num_kv_heads, int head_dim, int block_size, int num_blocks,
                               int elem_bytes, hipStream_t stream);

@@ -42,10 +42,12 @@ def pools_from_oracle(w, k_bits, v_bits):
         dev(v_bits if w.dtype == "bf16" else v_bits.view(np.float32))
 
 
-def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False):
+def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False, append=False):
     """The product path on one workload; returns a dict of device tensors.
     two_phase: decode with pa_decode_partials + pa_decode_merge instead of
-    pa_decode (needs partition_size > 0)."""
+    pa_decode (needs partition_size > 0).  append: the step's rows are written
+    by pa_append_decode(_partials) instead of pa_write_kv (every workload
+    writes each sequence's row at position L - 1)."""
     dt = torch_dtype(w)
     k, v = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, dt,
                              device, fill=float("nan"))
@@ -56,9 +58,29 @@ def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False):
         pa.copy_blocks(k, v, dev(w.copy_pairs))
     bt = dev(w.block_tables)
     new_slots = pa.slot_mapping(bt, dev(w.new_seq), dev(w.new_pos), w.block_size)
-    pa.write_kv(k, v, dev(w.new_key), dev(w.new_value), new_slots)
     cl = dev(w.context_lens)
     q = dev(w.q)
+    if append:
+        assert np.array_equal(w.new_seq, np.arange(w.num_seqs))
+        assert np.array_equal(w.new_pos, w.context_lens - 1)
+        nk, nv = dev(w.new_key), dev(w.new_value)
+        if two_phase:
+            ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
+                                    w.max_context_len, partition_size, device)
+            out = torch.empty_like(q)
+            pa.append_decode_partials(q, nk, nv, k, v, bt, cl, w.max_context_len, w.scale,
+                                      partition_size, ws, out)
+            pa.decode_merge(out, cl, w.num_kv_heads, w.block_size, w.max_blocks_per_seq,
+                            w.max_context_len, partition_size, ws)
+        else:
+            out = pa.append_decode(q, nk, nv, k, v, bt, cl, w.max_context_len, w.scale,
+                                   partition_size=partition_size)
+        torch.cuda.synchronize()
+        r = {"out": out, "hist_slots": hist_slots, "new_slots": new_slots, "bt": bt, "cl": cl}
+        if keep:
+            r["k"], r["v"] = k, v
+        return r
+    pa.write_kv(k, v, dev(w.new_key), dev(w.new_value), new_slots)
     if two_phase:
         ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
                                 w.max_context_len, partition_size, device)

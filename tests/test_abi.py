@@ -132,3 +132,29 @@ def test_workspace_size_formula(lib):
         assert pa.decode_workspace_bytes(*args) == expect(*args), args
     assert pa.decode_workspace_bytes(4, 30, 8, 128, 1024, 512) == 0
     assert pa.decode_workspace_bytes(4, 32, 8, 128, 1024, 0) == 0
+
+
+def append_call(lib, fn="pa_append_decode", **kw):
+    args = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=4,
+                Hq=32, Hkv=8, D=128, B=16, NB=100, MB=64, maxlen=1024, scale=0.088, P=0, ws=None,
+                wsb=0, dtype=BF16)
+    args.update(kw)
+    a = args
+    return getattr(lib, fn)(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["bt"],
+                            a["cl"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["MB"],
+                            a["maxlen"], a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["pa_append_decode", "pa_append_decode_partials"])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(key=None), INVALID),
+    (dict(value=None), INVALID),
+    (dict(key=FAKE_MISALIGNED), INVALID),
+    (dict(Hq=30, Hkv=8), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(P=512), WORKSPACE),
+    (dict(S=0), OK),
+    (dict(S=0, key=None, value=None), OK),
+])
+def test_append_decode_rejects_before_launch(lib, fn, kw, expect):
+    assert append_call(lib, fn, **kw) == expect

@@ -23,12 +23,13 @@ def _say(msg):
 
 
 def _check_step(w, partition_size, seqs=None, kv_heads=None, check_pool=True, two_phase=False,
-                ref=None):
+                ref=None, append=False):
     _say(f"{w.name} S={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
-         f"B={w.block_size} {w.dtype} P={partition_size}" + (" two-phase" if two_phase else ""))
+         f"B={w.block_size} {w.dtype} P={partition_size}" + (" two-phase" if two_phase else "")
+         + (" append" if append else ""))
     if ref is None:
         ref = oracle.run_step(w, seqs=seqs, kv_heads=kv_heads)
-    r = run_step(w, partition_size, keep=True, two_phase=two_phase)
+    r = run_step(w, partition_size, keep=True, two_phase=two_phase, append=append)
     assert np.array_equal(bits(r["hist_slots"]), ref["hist_slots"])
     assert np.array_equal(bits(r["new_slots"]), ref["new_slots"])
     if check_pool:
@@ -43,13 +44,18 @@ def _check_step(w, partition_size, seqs=None, kv_heads=None, check_pool=True, tw
 
 @pytest.mark.parametrize("P", [0, 16, 32, 64])
 def test_tiny_f32(P):
-    _check_step(W.tiny_f32(), P)
+    w = W.tiny_f32()
+    ref = oracle.run_step(w)
+    _check_step(w, P, ref=ref)
+    _check_step(w, P, ref=ref, append=True)
 
 
 @pytest.mark.parametrize("P", [0, 16, 48])
 def test_tiny_shape_bf16(P):
     w = W.custom([1, 17, 40, 100], 4, 2, 64, 16, "bf16", seed=307_011, name="tiny_bf16")
-    _check_step(w, P)
+    ref = oracle.run_step(w)
+    _check_step(w, P, ref=ref)
+    _check_step(w, P, ref=ref, append=True)
 
 
 RAGGED = list(range(1, 41)) + [63, 64, 65, 127, 128, 129, 255, 257, 511, 512, 513, 700]
@@ -69,8 +75,11 @@ def test_ragged_lengths(shape):
     ref = oracle.run_step(w)
     for P in (0, max(32, B), 512):
         _check_step(w, P, ref=ref)
-    if dt == "bf16":  # pa_decode is one launch for bf16; check the two-launch form too
-        _check_step(w, max(32, B), ref=ref, two_phase=True)
+    _check_step(w, max(32, B), ref=ref, two_phase=True)
+    # the appending step: the decode writes each sequence's row itself
+    for P in (0, max(32, B)):
+        _check_step(w, P, ref=ref, append=True)
+    _check_step(w, 512, ref=ref, append=True, two_phase=True)
 
 
 def test_two_phase_and_one_launch_agree():
@@ -134,6 +143,34 @@ def test_zero_and_short_lengths_decode(dt):
         out = pa.decode(dev(w.q), k, v, dev(w.block_tables), dev(lens), int(lens.max()), w.scale,
                         partition_size=P)
         torch.cuda.synchronize()
+        got = as_f64(out)
+        assert np.all(got[[0, 2]] == 0.0)
+        assert np.max(np.abs(got - want)) <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_append_with_zero_and_short_lengths(dt):
+    """pa_append_decode on the oracle's pool with some lengths cut to 0 and
+    others shortened: each sequence with L > 0 gets its row at position
+    L - 1 (bit-exact pools), L = 0 writes nothing and gives zeros."""
+    w = W.custom([30, 70, 1, 200, 16], 8, 2, 64, 16, dt, seed=307_042)
+    base = oracle.run_step(w)
+    lens = np.array([0, 33, 0, 129, 16], np.int32)
+    live = np.nonzero(lens > 0)[0].astype(np.int32)
+    for P in (0, 16, 64):
+        _say(f"append zero/short lengths {dt} P={P}")
+        kb, vb = base["k_pool"].copy(), base["v_pool"].copy()
+        slots = oracle.slot_mapping(w.block_tables, live, lens[live] - 1, w.block_size)
+        oracle.write_kv(kb, vb, oracle.to_bits(w.new_key, dt)[live],
+                        oracle.to_bits(w.new_value, dt)[live], slots, w.block_size)
+        want = oracle.decode(oracle.to_bits(w.q, dt), kb, vb, w.block_tables, lens, w.scale,
+                             w.num_kv_heads, w.block_size, dt)
+        k, v = pools_from_oracle(w, base["k_pool"], base["v_pool"])
+        out = pa.append_decode(dev(w.q), dev(w.new_key), dev(w.new_value), k, v,
+                               dev(w.block_tables), dev(lens), int(lens.max()), w.scale,
+                               partition_size=P)
+        torch.cuda.synchronize()
+        assert_pool_equal(w, k, v, kb, vb)
         got = as_f64(out)
         assert np.all(got[[0, 2]] == 0.0)
         assert np.max(np.abs(got - want)) <= TOL[dt]
@@ -213,6 +250,8 @@ def test_full_llama3_8b_decode():
     for P in (0, 512, 8192):
         _check_step(w, P, check_pool=(P == 0), ref=ref)
     _check_step(w, 512, check_pool=False, ref=ref, two_phase=True)
+    # the benchmark's step: appending partials (4096) + merge, pool checked bit for bit
+    _check_step(w, 4096, ref=ref, append=True, two_phase=True)
 
 
 def test_full_long_context_split():
@@ -221,12 +260,16 @@ def test_full_long_context_split():
     for two_phase in (False, True):
         _check_step(w, 512, seqs=range(w.num_seqs), kv_heads=[0, 5], check_pool=False,
                     two_phase=two_phase, ref=ref)
+    _check_step(w, 512, seqs=range(w.num_seqs), kv_heads=[0, 5], check_pool=False, ref=ref,
+                append=True)
 
 
 @pytest.mark.parametrize("phase", ["fork", "steady", "aligned"])
 def test_full_shared_prefix(phase):
     w = W.shared_prefix(phase)
-    _check_step(w, 512)
+    ref = oracle.run_step(w)
+    _check_step(w, 512, ref=ref)
+    _check_step(w, 4096, ref=ref, append=True)
 
 
 def test_full_mixed_lengths_block_sweep():
