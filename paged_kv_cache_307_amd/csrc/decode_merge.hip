@@ -9,9 +9,9 @@
 // launch carry its epoch stamp.  Pairs written whole by one worker are left
 // alone; pairs of length 0 get zeros.
 //
-// One 256-thread workgroup per (sequence, query head).  Thread t handles the
-// 16-byte dim chunk t % (D/4) of every (1024/D)-th record, so each load is a
-// coalesced float4; the partial sums meet in LDS.
+// One wave per (sequence, query head).  Lane t handles the 16-byte dim
+// chunk t % (D/4) of every (256/D)-th record, so each load is a coalesced
+// float4; the lane groups' partial sums meet through lane shuffles.
 
 #include <math.h>
 
@@ -22,7 +22,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 64;  // one wave per (sequence, query head)
 
 template <typename Elem>
 __device__ __forceinline__ Elem from_f32(float f);
@@ -44,18 +44,20 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float4 v) {
 
 template <typename Elem, int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
-  constexpr int CH = D / 4;             // float4 chunks per head
-  constexpr int PG = kThreads / CH;     // record groups
+  constexpr int CH = D / 4 < kThreads ? D / 4 : kThreads;  // float4 chunks per lane group
+  constexpr int CPL = D / 4 / CH;                          // chunks per lane (1 up to D = 256)
+  constexpr int PG = kThreads / CH;                        // record groups in the wave
   const int sh = blockIdx.x;
   const int h = sh % a.num_heads;
   const int s = sh / a.num_heads;
   const int G = a.group;
   const int kvh = h / G;
   const int hl = h % G;
+  const int lane = threadIdx.x;
   Elem* out = static_cast<Elem*>(a.out) + (int64_t(s) * a.num_heads + h) * D;
   PairRecords pr;
   if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
-    for (int i = threadIdx.x; i < D; i += kThreads) out[i] = from_f32<Elem>(0.f);
+    for (int i = lane; i < D; i += kThreads) out[i] = from_f32<Elem>(0.f);
     return;
   }
   if (pr.whole) return;  // written whole by its worker
@@ -63,27 +65,32 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
   const float* base = a.ws + pr.first * R;
   const int count = int(pr.last - pr.first + 1);
 
-  // One pass: thread (pg, c) folds records pg, pg + PG, ... into a running
-  // (max, denominator, numerator chunk c), rescaling when the max grows.
-  // The loads of kUnroll records are issued together and unconditionally
-  // (a stamp from another launch only drops the record afterwards), so a
-  // pair costs one round trip to memory per kUnroll records per thread.
+  // One pass: lane (pg, c) folds records pg, pg + PG, ... into a running
+  // (max, denominator, numerator chunks c, c + CH, ...), rescaling when the
+  // max grows.  The loads of kUnroll records are issued together and
+  // unconditionally (a stamp from another launch only drops the record
+  // afterwards), so a pair costs one round trip to memory per kUnroll
+  // records per lane.
   constexpr int kUnroll = 2;
-  const int c = threadIdx.x % CH;
-  const int pg = threadIdx.x / CH;
+  const int c = lane % CH;
+  const int pg = lane / CH;
   float m_t = -INFINITY, den_t = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 num[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) num[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int q0 = pg; q0 < count; q0 += PG * kUnroll) {
     uint32_t st[kUnroll];
     float mq[kUnroll], lq[kUnroll];
-    float4 oq[kUnroll];
+    float4 oq[kUnroll][CPL];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const float* rec = base + int64_t(min(q0 + u * PG, count - 1)) * R;
       st[u] = __float_as_uint(rec[G * D + 2 * G]);
       mq[u] = rec[G * D + hl];
       lq[u] = rec[G * D + G + hl];
-      oq[u] = *reinterpret_cast<const float4*>(rec + hl * D + 4 * c);
+#pragma unroll
+      for (int i = 0; i < CPL; ++i)
+        oq[u][i] = *reinterpret_cast<const float4*>(rec + hl * D + 4 * (c + CH * i));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -91,45 +98,66 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
       if (mq[u] > m_t) {
         const float r = exp2f(m_t - mq[u]);  // 0 on the first record
         den_t *= r;
-        num.x *= r; num.y *= r; num.z *= r; num.w *= r;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          num[i].x *= r; num[i].y *= r; num[i].z *= r; num[i].w *= r;
+        }
         m_t = mq[u];
       }
       const float w = exp2f(mq[u] - m_t);
       den_t += w * lq[u];
-      num.x += w * oq[u].x;
-      num.y += w * oq[u].y;
-      num.z += w * oq[u].z;
-      num.w += w * oq[u].w;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        num[i].x += w * oq[u][i].x;
+        num[i].y += w * oq[u][i].y;
+        num[i].z += w * oq[u][i].z;
+        num[i].w += w * oq[u][i].w;
+      }
     }
   }
-  __shared__ float sm_m[PG];
-  __shared__ float sm_den[PG];
-  __shared__ float4 sm_num[PG][CH];
-  if (c == 0) {
-    sm_m[pg] = m_t;
-    sm_den[pg] = den_t;
-  }
-  sm_num[pg][c] = num;
-  __syncthreads();
-  if (threadIdx.x < CH) {
-    float M = -INFINITY;
+  // Fold the record groups (lanes c, c + CH, ...) into group 0.  A group
+  // that saw no record has den == 0 (a record has l >= 1, or NaN when a
+  // broken block id poisoned it, which must propagate).
 #pragma unroll
-    for (int g = 0; g < PG; ++g) M = fmaxf(M, sm_m[g]);
-    float den = 0.f;
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int off = CH; off < kThreads; off <<= 1) {
+    const float m_o = __shfl_xor(m_t, off);
+    const float den_o = __shfl_xor(den_t, off);
+    float4 num_o[CPL];
 #pragma unroll
-    for (int g = 0; g < PG; ++g) {
-      // a group that saw no record has den == 0 (a record has l >= 1, or
-      // NaN when a broken block id poisoned it, which must propagate)
-      if (sm_den[g] == 0.f) continue;
-      const float w = exp2f(sm_m[g] - M);
-      den += w * sm_den[g];
-      const float4 u = sm_num[g][c];
-      t.x += w * u.x; t.y += w * u.y; t.z += w * u.z; t.w += w * u.w;
+    for (int i = 0; i < CPL; ++i) {
+      num_o[i].x = __shfl_xor(num[i].x, off);
+      num_o[i].y = __shfl_xor(num[i].y, off);
+      num_o[i].z = __shfl_xor(num[i].z, off);
+      num_o[i].w = __shfl_xor(num[i].w, off);
     }
-    const float inv = 1.0f / den;
-    t.x *= inv; t.y *= inv; t.z *= inv; t.w *= inv;
-    store4<Elem>(out + 4 * c, t);
+    if (den_o == 0.f) continue;  // same decision in every lane of the pair of groups
+    if (den_t == 0.f) {
+      m_t = m_o;
+      den_t = den_o;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) num[i] = num_o[i];
+      continue;
+    }
+    const float M = fmaxf(m_t, m_o);
+    const float w = exp2f(m_t - M), wo = exp2f(m_o - M);
+    den_t = w * den_t + wo * den_o;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      num[i].x = w * num[i].x + wo * num_o[i].x;
+      num[i].y = w * num[i].y + wo * num_o[i].y;
+      num[i].z = w * num[i].z + wo * num_o[i].z;
+      num[i].w = w * num[i].w + wo * num_o[i].w;
+    }
+    m_t = M;
+  }
+  if (pg == 0) {
+    const float inv = 1.0f / den_t;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      float4 t = num[i];
+      t.x *= inv; t.y *= inv; t.z *= inv; t.w *= inv;
+      store4<Elem>(out + 4 * (c + CH * i), t);
+    }
   }
 }
 
