@@ -9,9 +9,10 @@
 // launch carry its epoch stamp.  Pairs written whole by one worker are left
 // alone; pairs of length 0 get zeros.
 //
-// One wave per (sequence, query head).  Lane t handles the 16-byte dim
-// chunk t % (D/4) of every (256/D)-th record, so each load is a coalesced
-// float4; the lane groups' partial sums meet through lane shuffles.
+// One workgroup of one or four waves per (sequence, query head).  In each
+// wave, lane t handles the 16-byte dim chunk t % (D/4) of every
+// (256/D)-th record, so each load is a coalesced float4; the lane groups'
+// partial sums meet through lane shuffles, and the waves' through LDS.
 
 #include <math.h>
 
@@ -22,7 +23,7 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 64;  // one wave per (sequence, query head)
+constexpr int kThreads = 64;  // lanes per wave
 
 template <typename Elem>
 __device__ __forceinline__ Elem from_f32(float f);
@@ -42,22 +43,55 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float4 v) {
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
-template <typename Elem, int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
+// Running log-sum-exp state of a lane: max, denominator, numerator chunks.
+template <int CPL>
+struct Fold {
+  float m, den;
+  float4 num[CPL];
+};
+
+// a <- a (+) b.  A state that saw no record has den == 0 (a record has
+// l >= 1, or NaN when a broken block id poisoned it, which must propagate).
+template <int CPL>
+__device__ __forceinline__ void fold_into(Fold<CPL>& a, const Fold<CPL>& b) {
+  if (b.den == 0.f) return;
+  if (a.den == 0.f) {
+    a = b;
+    return;
+  }
+  const float M = fmaxf(a.m, b.m);
+  const float wa = exp2f(a.m - M), wb = exp2f(b.m - M);
+  a.den = wa * a.den + wb * b.den;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    a.num[i].x = wa * a.num[i].x + wb * b.num[i].x;
+    a.num[i].y = wa * a.num[i].y + wb * b.num[i].y;
+    a.num[i].z = wa * a.num[i].z + wb * b.num[i].z;
+    a.num[i].w = wa * a.num[i].w + wb * b.num[i].w;
+  }
+  a.m = M;
+}
+
+// NW waves per (sequence, query head): one wave for pairs with few records,
+// four when partitions are many.
+template <typename Elem, int D, int NW>
+__global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int B) {
   constexpr int CH = D / 4 < kThreads ? D / 4 : kThreads;  // float4 chunks per lane group
   constexpr int CPL = D / 4 / CH;                          // chunks per lane (1 up to D = 256)
-  constexpr int PG = kThreads / CH;                        // record groups in the wave
+  constexpr int GPW = kThreads / CH;                       // record groups per wave
+  constexpr int PG = GPW * NW;                             // record groups in the workgroup
   const int sh = blockIdx.x;
   const int h = sh % a.num_heads;
   const int s = sh / a.num_heads;
   const int G = a.group;
   const int kvh = h / G;
   const int hl = h % G;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kThreads;
+  const int wave = threadIdx.x / kThreads;
   Elem* out = static_cast<Elem*>(a.out) + (int64_t(s) * a.num_heads + h) * D;
   PairRecords pr;
   if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
-    for (int i = lane; i < D; i += kThreads) out[i] = from_f32<Elem>(0.f);
+    for (int i = threadIdx.x; i < D; i += kThreads * NW) out[i] = from_f32<Elem>(0.f);
     return;
   }
   if (pr.whole) return;  // written whole by its worker
@@ -73,11 +107,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
   // records per lane.
   constexpr int kUnroll = 2;
   const int c = lane % CH;
-  const int pg = lane / CH;
-  float m_t = -INFINITY, den_t = 0.f;
-  float4 num[CPL];
+  const int pg = wave * GPW + lane / CH;
+  Fold<CPL> f;
+  f.m = -INFINITY;
+  f.den = 0.f;
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) num[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < CPL; ++i) f.num[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int q0 = pg; q0 < count; q0 += PG * kUnroll) {
     uint32_t st[kUnroll];
     float mq[kUnroll], lq[kUnroll];
@@ -95,79 +130,80 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a, int B) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       if (q0 + u * PG >= count || st[u] != pr.epoch) continue;
-      if (mq[u] > m_t) {
-        const float r = exp2f(m_t - mq[u]);  // 0 on the first record
-        den_t *= r;
+      if (mq[u] > f.m) {
+        const float r = exp2f(f.m - mq[u]);  // 0 on the first record
+        f.den *= r;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
-          num[i].x *= r; num[i].y *= r; num[i].z *= r; num[i].w *= r;
+          f.num[i].x *= r; f.num[i].y *= r; f.num[i].z *= r; f.num[i].w *= r;
         }
-        m_t = mq[u];
+        f.m = mq[u];
       }
-      const float w = exp2f(mq[u] - m_t);
-      den_t += w * lq[u];
+      const float w = exp2f(mq[u] - f.m);
+      f.den += w * lq[u];
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        num[i].x += w * oq[u][i].x;
-        num[i].y += w * oq[u][i].y;
-        num[i].z += w * oq[u][i].z;
-        num[i].w += w * oq[u][i].w;
+        f.num[i].x += w * oq[u][i].x;
+        f.num[i].y += w * oq[u][i].y;
+        f.num[i].z += w * oq[u][i].z;
+        f.num[i].w += w * oq[u][i].w;
       }
     }
   }
-  // Fold the record groups (lanes c, c + CH, ...) into group 0.  A group
-  // that saw no record has den == 0 (a record has l >= 1, or NaN when a
-  // broken block id poisoned it, which must propagate).
+  // Fold the wave's record groups (lanes c, c + CH, ...) together through
+  // lane shuffles; every lane of a chunk ends with the wave's state.
 #pragma unroll
   for (int off = CH; off < kThreads; off <<= 1) {
-    const float m_o = __shfl_xor(m_t, off);
-    const float den_o = __shfl_xor(den_t, off);
-    float4 num_o[CPL];
+    Fold<CPL> o;
+    o.m = __shfl_xor(f.m, off);
+    o.den = __shfl_xor(f.den, off);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      num_o[i].x = __shfl_xor(num[i].x, off);
-      num_o[i].y = __shfl_xor(num[i].y, off);
-      num_o[i].z = __shfl_xor(num[i].z, off);
-      num_o[i].w = __shfl_xor(num[i].w, off);
+      o.num[i].x = __shfl_xor(f.num[i].x, off);
+      o.num[i].y = __shfl_xor(f.num[i].y, off);
+      o.num[i].z = __shfl_xor(f.num[i].z, off);
+      o.num[i].w = __shfl_xor(f.num[i].w, off);
     }
-    if (den_o == 0.f) continue;  // same decision in every lane of the pair of groups
-    if (den_t == 0.f) {
-      m_t = m_o;
-      den_t = den_o;
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) num[i] = num_o[i];
-      continue;
-    }
-    const float M = fmaxf(m_t, m_o);
-    const float w = exp2f(m_t - M), wo = exp2f(m_o - M);
-    den_t = w * den_t + wo * den_o;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      num[i].x = w * num[i].x + wo * num_o[i].x;
-      num[i].y = w * num[i].y + wo * num_o[i].y;
-      num[i].z = w * num[i].z + wo * num_o[i].z;
-      num[i].w = w * num[i].w + wo * num_o[i].w;
-    }
-    m_t = M;
+    fold_into(f, o);
   }
-  if (pg == 0) {
-    const float inv = 1.0f / den_t;
+  if constexpr (NW > 1) {  // then the waves' states through LDS
+    __shared__ Fold<CPL> part[NW][CH];
+    if (lane < CH) part[wave][lane] = f;
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+      if (lane < CH) fold_into(f, part[w][lane]);
+  }
+  if (lane < CH) {
+    const float inv = 1.0f / f.den;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      float4 t = num[i];
+      float4 t = f.num[i];
       t.x *= inv; t.y *= inv; t.z *= inv; t.w *= inv;
       store4<Elem>(out + 4 * (c + CH * i), t);
     }
   }
 }
 
+// Waves per (sequence, query head) in the merge: one while a pair's records
+// fit in a couple of rounds of loads, four for long runs of partitions.
+constexpr int kWideMergeParts = 8;
+
+template <typename Elem, int D>
+hipError_t launch_merge_d(const DecodeArgs& a, int block_size, hipStream_t stream) {
+  const dim3 grid(unsigned(int64_t(a.num_seqs) * a.num_heads));
+  if (a.max_partitions > kWideMergeParts)
+    return launch(merge_kernel<Elem, D, 4>, grid, dim3(4 * kThreads), 0, stream, a, block_size);
+  return launch(merge_kernel<Elem, D, 1>, grid, dim3(kThreads), 0, stream, a, block_size);
+}
+
 template <typename Elem>
 hipError_t launch_merge_elem(const DecodeArgs& a, int head_dim, int block_size, hipStream_t stream) {
-  const dim3 grid(unsigned(int64_t(a.num_seqs) * a.num_heads));
   switch (head_dim) {
-    case 64: return launch(merge_kernel<Elem, 64>, grid, dim3(kThreads), 0, stream, a, block_size);
-    case 128: return launch(merge_kernel<Elem, 128>, grid, dim3(kThreads), 0, stream, a, block_size);
-    case 256: return launch(merge_kernel<Elem, 256>, grid, dim3(kThreads), 0, stream, a, block_size);
+    case 64: return launch_merge_d<Elem, 64>(a, block_size, stream);
+    case 128: return launch_merge_d<Elem, 128>(a, block_size, stream);
+    case 256: return launch_merge_d<Elem, 256>(a, block_size, stream);
     default: return hipErrorInvalidValue;
   }
 }
