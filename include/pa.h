@@ -191,7 +191,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * smaller.  Table entries at or past ceil(L_s / B) are never read.  Slots of
  * the last block past L_s are never used (they may hold anything, NaN
  * included).  Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED /
- * PA_ERR_WORKSPACE on a failed check.
+ * PA_ERR_WORKSPACE on a failed check; with partition_size > 0,
+ * PA_ERR_UNSUPPORTED also when num_seqs * ceil(max_context_len / 16)
+ * exceeds 2^31 - 1 (the split schedule counts tiles in 32-bit integers).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,

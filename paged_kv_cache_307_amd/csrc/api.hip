@@ -140,6 +140,9 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
   if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
 
   const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
+  // the split schedule sums 16-token tiles over sequences in 32-bit integers
+  if (partition_size > 0 && int64_t(num_seqs) * ((max_len + 15) / 16) > 0x7FFFFFFF)
+    return PA_ERR_UNSUPPORTED;
   DecodeArgs& a = plan->args;
   plan->split = partition_size > 0;
   if (plan->split) {
@@ -312,6 +315,7 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
       int64_t(workspace_bytes) < workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts))
     return PA_ERR_WORKSPACE;
   if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  if (int64_t(num_seqs) * ((max_len + 15) / 16) > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
   const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size);
   if (workers <= 0) return PA_ERR_HIP;
   DecodeArgs a{};

@@ -49,12 +49,15 @@ struct PairShape {
   int parts;   // nparts_s
 };
 
-__device__ __forceinline__ PairShape pair_shape(const DecodeArgs& a, int s, int block_size) {
-  const int L = effective_len(a, s, block_size);
+__device__ __forceinline__ PairShape shape_of_len(const DecodeArgs& a, int L) {
   PairShape p;
   p.tiles = (L + 15) / 16;
   p.parts = (L + a.partition_size - 1) / a.partition_size;
   return p;
+}
+
+__device__ __forceinline__ PairShape pair_shape(const DecodeArgs& a, int s, int block_size) {
+  return shape_of_len(a, effective_len(a, s, block_size));
 }
 
 // Inclusive wave-wide prefix sum of a 32-bit value.
@@ -73,6 +76,7 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 struct Slice {
   int64_t n, x0, x1;
   int seq;          // sequence holding x0 (valid when x0 < x1)
+  int len;          // its effective length
   int64_t pref_t;   // prefT[seq]
   int64_t pref_p;   // prefP[seq]
 };
@@ -101,17 +105,19 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
   r.x1 = r.n > 0 ? slice_start(r.n, a.workers, b + 1) : 0;
   const bool publish = b == 0;
   int32_t* meta = reinterpret_cast<int32_t*>(a.ws_meta);
-  int found_s = -1;
+  int found_s = -1, found_len = 0;
   int64_t found_t = 0, found_p = 0;
   int64_t ct = it - lt, cp = ip - lp;
   for (int s = first; s < last; ++s) {
-    const PairShape ps = pair_shape(a, s, block_size);
+    const int len = effective_len(a, s, block_size);
+    const PairShape ps = shape_of_len(a, len);
     if (publish) {
       meta[s] = int32_t(ct);
       meta[S + s] = int32_t(cp);
     }
     if (ps.tiles > 0 && r.x0 >= ct * a.num_kv_heads && r.x0 < (ct + ps.tiles) * a.num_kv_heads) {
       found_s = s;
+      found_len = len;
       found_t = ct;
       found_p = cp;
     }
@@ -125,6 +131,7 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
   const unsigned long long owner = __ballot(found_s >= 0);
   const int src = owner ? int(__builtin_ctzll(owner)) : 0;
   r.seq = wave_uniform(__shfl(found_s, src));
+  r.len = wave_uniform(__shfl(found_len, src));
   r.pref_t = wave_uniform64(__shfl(found_t, src));
   r.pref_p = wave_uniform64(__shfl(found_p, src));
   return r;
@@ -142,14 +149,20 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, 
   int s = sl.seq;
   int64_t sbase = sl.pref_t * Hkv;        // line start of sequence s
   int64_t gpb = sl.pref_p * Hkv;          // first partition index of sequence s
-  PairShape ps = pair_shape(a, s, block_size);
+  // the current sequence's length comes from the scan; the next one's is
+  // fetched a sequence ahead
+  int len = sl.len;
+  int len_next = s + 1 < a.num_seqs ? effective_len(a, s + 1, block_size) : 0;
+  PairShape ps = shape_of_len(a, len);
   int64_t cur = sl.x0;
   while (cur < sl.x1) {
     if (cur >= sbase + int64_t(Hkv) * ps.tiles) {
       sbase += int64_t(Hkv) * ps.tiles;
       gpb += int64_t(Hkv) * ps.parts;
       ++s;
-      ps = pair_shape(a, s, block_size);
+      len = len_next;
+      len_next = s + 1 < a.num_seqs ? effective_len(a, s + 1, block_size) : 0;
+      ps = shape_of_len(a, len);
       continue;
     }
     const int64_t off = cur - sbase;
@@ -162,7 +175,7 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, 
     const int ntile = int(end - cur);
     const bool whole = tin == 0 && ntile == ps.tiles;
     const int64_t rec = gpb + int64_t(g) * ps.parts + part + b;
-    piece(s, g, effective_len(a, s, block_size), tin, ntile, whole, rec);
+    piece(s, g, len, tin, ntile, whole, rec);
     cur = end;
   }
 }

@@ -80,6 +80,8 @@ def decode_call(lib, fn="pa_decode", **kw):
     (dict(P=512, ws=FAKE_MISALIGNED, wsb=1 << 30), WORKSPACE),
     (dict(S=0), OK),                          # nothing to do: no launch
     (dict(S=0, out=None, q=None), OK),
+    # split schedule: sequences x 16-token tiles must fit in 31 bits
+    (dict(S=1 << 20, MB=4096, maxlen=1 << 16, P=512, ws=FAKE, wsb=1 << 40), UNSUPPORTED),
 ])
 def test_decode_rejects_before_launch(lib, fn, kw, expect):
     assert decode_call(lib, fn, **kw) == expect
