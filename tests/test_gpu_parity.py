@@ -176,6 +176,50 @@ def test_append_with_zero_and_short_lengths(dt):
         assert np.max(np.abs(got - want)) <= TOL[dt]
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_context_lens_clamped(dt):
+    """context_lens beyond max_context_len, or beyond the table's capacity
+    (max_blocks_per_seq * B = 112 here, every row full), are clamped to the
+    smaller bound."""
+    w = W.custom([112, 112, 112, 112], 8, 2, 64, 16, dt, seed=307_043)
+    ref = oracle.run_step(w)
+    k, v = pools_from_oracle(w, ref["k_pool"], ref["v_pool"])
+    cap = w.max_blocks_per_seq * w.block_size
+    assert cap == 112
+    lens = np.array([40, 500, 100, 10_000], np.int32)
+    for max_len in (80, 200):                       # below and above the capacity
+        eff = np.minimum(np.minimum(lens, max_len), cap).astype(np.int32)
+        want = oracle.decode(oracle.to_bits(w.q, dt), ref["k_pool"], ref["v_pool"],
+                             w.block_tables, eff, w.scale, w.num_kv_heads, w.block_size, dt)
+        for P in (0, 32):
+            _say(f"clamped lengths {dt} max_len={max_len} P={P}")
+            out = pa.decode(dev(w.q), k, v, dev(w.block_tables), dev(lens), max_len, w.scale,
+                            partition_size=P)
+            torch.cuda.synchronize()
+            assert np.max(np.abs(as_f64(out) - want)) <= TOL[dt]
+
+
+def test_side_stream_and_repeat_are_bit_identical():
+    """The ABI runs on the caller's stream: a decode on a side stream gives
+    the same bits as on the default stream, and repeating a launch
+    reproduces them (the schedule and the merge order are deterministic)."""
+    w = W.custom([5, 100, 600, 1500, 17], 32, 8, 128, 16, "bf16", seed=307_044)
+    r = run_step(w, 0, keep=True)
+    q = dev(w.q)
+    args = (q, r["k"], r["v"], r["bt"], r["cl"], w.max_context_len, w.scale)
+    base = pa.decode(*args, partition_size=64)
+    again = pa.decode(*args, partition_size=64)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        other = pa.decode(*args, partition_size=64)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(base, again) and torch.equal(base, other)
+    ref = oracle.run_step(w)["out"]
+    assert np.max(np.abs(as_f64(base) - ref)) <= TOL["bf16"]
+
+
 def test_single_token_is_exact_copy():
     """L = 1: the output is the token's V row, bit for bit after rounding."""
     w = W.custom([1, 1, 1], 8, 4, 128, 16, "bf16", seed=307_051)
