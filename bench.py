@@ -11,6 +11,10 @@ With --separate-write the rows go through pa_write_kv first and the decode
 is pa_decode_partials + pa_decode_merge.  The partition size defaults to one at least as long as the
 workload's longest context (so records only arise where a worker's slice
 cuts a pair); the long-context workload keeps its 512-token partitions.
+When the workload's block tables share blocks between sequences (the
+shared-prefix workloads) the decode gets PA_DECODE_SHARED_BLOCKS, so shared
+blocks stay cacheable; otherwise K/V tiles are streamed (``--shared-blocks``
+overrides the choice).
 
 The default workload is the Llama-3-8B-shaped decode layer: 64 sequences,
 32 query / 8 KV heads, head_dim 128, bf16, B=16, context lengths uniform on
@@ -52,7 +56,7 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
                   "paged_kv_cache_307_amd/csrc/api.hip"]
 MEASURED_TRAFFIC = {
-    ("llama3_8b_decode", 4096, True): {
+    ("llama3_8b_decode", 4096, True, False): {
         "bytes": 546613614, "fetch_bytes": 541747043, "write_bytes": 4866572,
         "sources_sha256": "3b0120a45493730646f646ecec6741a7e8f81f504cb4a1f7014b275a9991f363"},
 }
@@ -95,10 +99,17 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload, partition, append):
+def shares_blocks(w):
+    """Whether some physical block is read by more than one sequence."""
+    ids = [w.block_tables[s, :-(-int(L) // w.block_size)] for s, L in enumerate(w.context_lens)]
+    ids = np.concatenate(ids) if ids else np.zeros(0, np.int32)
+    return len(np.unique(ids)) < len(ids)
+
+
+def measured_traffic(workload, partition, append, shared):
     """Counter-derived HBM bytes per launch, or None when there is no
     measurement for this workload and step or the kernel changed since."""
-    rec = MEASURED_TRAFFIC.get((workload, partition, append))
+    rec = MEASURED_TRAFFIC.get((workload, partition, append, shared))
     if rec is None or rec["sources_sha256"] != kernel_sources_sha256():
         return None
     return rec["bytes"]
@@ -167,6 +178,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate-write", action="store_true",
                     help="write the step's rows with pa_write_kv, then pa_decode_partials")
+    ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
+                    help="PA_DECODE_SHARED_BLOCKS: auto = when the tables share blocks")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks on a known byte count (profiler calibration)")
     args = ap.parse_args()
@@ -196,6 +209,7 @@ def main():
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     B = w.block_size
     P = default_partition if args.partition is None else args.partition
+    shared = shares_blocks(w) if args.shared_blocks == "auto" else args.shared_blocks == "on"
     hist_bt, bt, cl = t(w.hist_block_tables), t(w.block_tables), t(w.context_lens)
     k0, v0 = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, B, w.head_dim, dt, dev,
                                fill=float("nan"))
@@ -218,9 +232,10 @@ def main():
         if ev is not None:
             ev[0].record()
         if args.separate_write:
-            pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out)
+            pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out, shared_blocks=shared)
         else:
-            pa.append_decode_partials(q, new_k, new_v, k, v, bt, cl, mcl, w.scale, P, ws, out)
+            pa.append_decode_partials(q, new_k, new_v, k, v, bt, cl, mcl, w.scale, P, ws, out,
+                                      shared_blocks=shared)
         if ev is not None:
             ev[1].record()
         pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
@@ -280,6 +295,7 @@ def main():
             "context_len_min": int(L.min()), "context_len_max": int(L.max()),
             "context_len_mean": round(float(L.mean()), 1), "num_blocks": w.num_blocks,
             "partition_size": P, "layers_rotated": args.layers,
+            "kv_loads": "cached (PA_DECODE_SHARED_BLOCKS)" if shared else "streamed (nontemporal)",
             "step": ("pa_write_kv + pa_decode_partials + pa_decode_merge" if args.separate_write
                      else "pa_append_decode_partials + pa_decode_merge"),
         },
@@ -287,12 +303,12 @@ def main():
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
         "roofline": {
-            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true> (" +
+            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true,{str(not shared).lower()}> (" +
                       ("pa_decode_partials" if args.separate_write else "pa_append_decode_partials") + ")",
             "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(part_avg_ms * 1e3, 3), "bytes_per_launch": part_bytes,
-            "traffic": measured_traffic(w.name, P, not args.separate_write),
+            "traffic": measured_traffic(w.name, P, not args.separate_write, shared),
         },
         "cpu_baseline": cpu,
     }

@@ -80,6 +80,22 @@ enum {
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
 
+/*
+ * Decode flags (the `flags` argument of the decode entry points; other bits
+ * are rejected with PA_ERR_INVALID_ARG).
+ *
+ * PA_DECODE_SHARED_BLOCKS -- the launch reads some physical blocks from more
+ *   than one sequence (a shared prompt prefix, parallel samples or beams that
+ *   have not diverged; the pages' copy-on-write sharing).  The bf16 kernel
+ *   then reads K/V with the default cache policy, so that repeated reads of a
+ *   shared block can hit in the L2 or the last-level cache.  Without the flag
+ *   it reads K/V tiles as streamed, read-once data (the nontemporal policy),
+ *   which is faster when every block is read once per launch and slower when
+ *   blocks are shared.  Results are identical either way; the fp32 kernel
+ *   ignores the flag.
+ */
+enum { PA_DECODE_SHARED_BLOCKS = 1 };
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pa_status_string(int status);
 
@@ -183,6 +199,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  *                     log-sum-exp reduction.
  *   workspace, workspace_bytes  >= pa_decode_workspace_bytes(...) when
  *                     partition_size > 0; may be NULL/0 otherwise.
+ *   flags             0 or PA_DECODE_SHARED_BLOCKS (a cache hint, above)
  *
  * out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) V_t over t < L_s, with
  * K_t, V_t read from block block_tables[s][t / B] at offset t % B and KV head
@@ -200,7 +217,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
               int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
-              void* stream);
+              int32_t flags, void* stream);
 
 /*
  * pa_decode_partials / pa_decode_merge -- the two phases pa_decode runs when
@@ -216,7 +233,8 @@ int pa_decode_partials(void* out, const void* q, const void* k_cache, const void
                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                        int32_t max_context_len, float scale, int32_t partition_size,
-                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+                       void* workspace, size_t workspace_bytes, int32_t dtype, int32_t flags,
+                       void* stream);
 
 int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
@@ -251,7 +269,8 @@ int pa_append_decode(void* out, const void* q, const void* key, const void* valu
                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                      int32_t max_context_len, float scale, int32_t partition_size,
-                     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
+                     void* workspace, size_t workspace_bytes, int32_t dtype, int32_t flags,
+                     void* stream);
 
 int pa_append_decode_partials(void* out, const void* q, const void* key, const void* value,
                               void* k_cache, void* v_cache, const int32_t* block_tables,
@@ -260,7 +279,7 @@ int pa_append_decode_partials(void* out, const void* q, const void* key, const v
                               int32_t num_blocks, int32_t max_blocks_per_seq,
                               int32_t max_context_len, float scale, int32_t partition_size,
                               void* workspace, size_t workspace_bytes, int32_t dtype,
-                              void* stream);
+                              int32_t flags, void* stream);
 
 #ifdef __cplusplus
 }

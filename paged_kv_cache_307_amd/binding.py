@@ -52,15 +52,17 @@ def load_library():
         "pa_write_kv": (ctypes.c_int, [P, P, P, P, P, I, I, I, I, I, I, P]),
         "pa_copy_blocks": (ctypes.c_int, [P, P, P, I, I, I, I, I, I, P]),
         "pa_decode_workspace_bytes": (Z, [I, I, I, I, I, I]),
-        "pa_decode": (ctypes.c_int, [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, P]),
+        "pa_decode": (ctypes.c_int,
+                      [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, I, P]),
         "pa_decode_partials": (ctypes.c_int,
-                               [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, P]),
+                               [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, I, P]),
         "pa_decode_merge": (ctypes.c_int, [P, P, I, I, I, I, I, I, I, I, P, Z, I, P]),
         "pa_append_decode": (ctypes.c_int,
-                             [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, P]),
+                             [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, I,
+                              P]),
         "pa_append_decode_partials": (ctypes.c_int,
                                       [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z,
-                                       I, P]),
+                                       I, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -98,6 +100,13 @@ def _cuda_contig(name, t, dtype=None):
     _need(t.is_contiguous(), f"{name} must be contiguous")
     if dtype is not None:
         _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+
+
+PA_DECODE_SHARED_BLOCKS = 1
+
+
+def _flags(shared_blocks) -> int:
+    return PA_DECODE_SHARED_BLOCKS if shared_blocks else 0
 
 
 def _dtype_code(t) -> int:
@@ -212,8 +221,10 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-           partition_size=0, workspace=None, out=None, stream=None):
-    """out[s, h] = softmax(scale q.K^T) V over the paged context of sequence s."""
+           partition_size=0, workspace=None, out=None, stream=None, shared_blocks=False):
+    """out[s, h] = softmax(scale q.K^T) V over the paged context of sequence s.
+    shared_blocks: some blocks are read by more than one sequence (a cache
+    hint, PA_DECODE_SHARED_BLOCKS; results are the same either way)."""
     if out is None:
         out = torch.empty_like(q)
     dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
@@ -224,20 +235,20 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, sca
     st = load_library().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _ptr(workspace),
-        ws_bytes, _dtype_code(q), _stream(stream))
+        ws_bytes, _dtype_code(q), _flags(shared_blocks), _stream(stream))
     _check(st, "pa_decode")
     return out
 
 
 def decode_partials(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                    partition_size, workspace, out, stream=None):
+                    partition_size, workspace, out, stream=None, shared_blocks=False):
     dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
     s, hq, hkv, d, b, nb, mb, mcl = dims
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load_library().pa_decode_partials(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _ptr(workspace),
-        ws_bytes, _dtype_code(q), _stream(stream))
+        ws_bytes, _dtype_code(q), _flags(shared_blocks), _stream(stream))
     _check(st, "pa_decode_partials")
     return out
 
@@ -265,7 +276,8 @@ def _append_args(key, value, q, hkv, d):
 
 
 def append_decode(q, key, value, k_cache, v_cache, block_tables, context_lens, max_context_len,
-                  scale, partition_size=0, workspace=None, out=None, stream=None):
+                  scale, partition_size=0, workspace=None, out=None, stream=None,
+                  shared_blocks=False):
     """Store each sequence's new K/V row at position L - 1, then decode."""
     if out is None:
         out = torch.empty_like(q)
@@ -278,13 +290,15 @@ def append_decode(q, key, value, k_cache, v_cache, block_tables, context_lens, m
     st = load_library().pa_append_decode(
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, b, nb, mb, mcl, float(scale),
-        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream))
+        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _flags(shared_blocks),
+        _stream(stream))
     _check(st, "pa_append_decode")
     return out
 
 
 def append_decode_partials(q, key, value, k_cache, v_cache, block_tables, context_lens,
-                           max_context_len, scale, partition_size, workspace, out, stream=None):
+                           max_context_len, scale, partition_size, workspace, out, stream=None,
+                           shared_blocks=False):
     dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
     s, hq, hkv, d, b, nb, mb, mcl = dims
     _append_args(key, value, q, hkv, d)
@@ -292,6 +306,7 @@ def append_decode_partials(q, key, value, k_cache, v_cache, block_tables, contex
     st = load_library().pa_append_decode_partials(
         _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
         _ptr(block_tables), _ptr(context_lens), s, hq, hkv, d, b, nb, mb, mcl, float(scale),
-        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _stream(stream))
+        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _flags(shared_blocks),
+        _stream(stream))
     _check(st, "pa_append_decode_partials")
     return out

@@ -118,7 +118,8 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                 int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                size_t workspace_bytes, int32_t dtype) {
+                size_t workspace_bytes, int32_t dtype, int32_t flags) {
+  if ((flags & ~int32_t(PA_DECODE_SHARED_BLOCKS)) != 0) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_blocks < 0 ||
       max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
     return PA_ERR_INVALID_ARG;
@@ -179,6 +180,7 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = int32_t(max_len);
   a.scale_log2e = scale * 1.4426950408889634f;
+  a.shared_blocks = (flags & PA_DECODE_SHARED_BLOCKS) ? 1 : 0;
   plan->head_dim = head_dim;
   plan->block_size = block_size;
   plan->bf16 = dtype == PA_DTYPE_BF16;
@@ -283,12 +285,13 @@ int pa_decode_partials(void* out, const void* q, const void* k_cache, const void
                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                        int32_t max_context_len, float scale, int32_t partition_size,
-                       void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+                       void* workspace, size_t workspace_bytes, int32_t dtype, int32_t flags,
+                       void* stream) {
   DecodePlan plan;
   const int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                              num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
-                             workspace_bytes, dtype);
+                             workspace_bytes, dtype, flags);
   if (st != PA_OK || plan.args.num_seqs == 0) return st;
   return status_of(launch_partials(plan, static_cast<hipStream_t>(stream)));
 }
@@ -343,12 +346,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
               int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
-              void* stream) {
+              int32_t flags, void* stream) {
   DecodePlan plan;
   const int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                              num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                              max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
-                             workspace_bytes, dtype);
+                             workspace_bytes, dtype, flags);
   if (st != PA_OK || plan.args.num_seqs == 0) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_partials(plan, s);
@@ -364,12 +367,12 @@ int pa_append_decode_partials(void* out, const void* q, const void* key, const v
                               int32_t num_blocks, int32_t max_blocks_per_seq,
                               int32_t max_context_len, float scale, int32_t partition_size,
                               void* workspace, size_t workspace_bytes, int32_t dtype,
-                              void* stream) {
+                              int32_t flags, void* stream) {
   DecodePlan plan;
   int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
-                       workspace_bytes, dtype);
+                       workspace_bytes, dtype, flags);
   if (st != PA_OK) return st;
   st = check_append(key, value, num_seqs);
   if (st != PA_OK || plan.args.num_seqs == 0) return st;
@@ -383,12 +386,13 @@ int pa_append_decode(void* out, const void* q, const void* key, const void* valu
                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                      int32_t max_context_len, float scale, int32_t partition_size,
-                     void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+                     void* workspace, size_t workspace_bytes, int32_t dtype, int32_t flags,
+                     void* stream) {
   DecodePlan plan;
   int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
-                       workspace_bytes, dtype);
+                       workspace_bytes, dtype, flags);
   if (st != PA_OK) return st;
   st = check_append(key, value, num_seqs);
   if (st != PA_OK || plan.args.num_seqs == 0) return st;

@@ -34,6 +34,7 @@ struct DecodeArgs {
   int32_t partition_size;     // tokens per partition (multiple of 16 and of B)
   int32_t max_partitions;     // ceil(max_context_len / partition_size), >= 1
   int32_t split;              // 1: balanced split-KV workers; 0: one wave per (seq, KV head)
+  int32_t shared_blocks;      // 1: blocks may be read by several sequences (default-cached loads)
   float scale_log2e;          // scale * log2(e)
 };
 

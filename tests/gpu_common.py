@@ -42,12 +42,14 @@ def pools_from_oracle(w, k_bits, v_bits):
         dev(v_bits if w.dtype == "bf16" else v_bits.view(np.float32))
 
 
-def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False, append=False):
+def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False, append=False,
+             shared_blocks=False):
     """The product path on one workload; returns a dict of device tensors.
     two_phase: decode with pa_decode_partials + pa_decode_merge instead of
     pa_decode (needs partition_size > 0).  append: the step's rows are written
     by pa_append_decode(_partials) instead of pa_write_kv (every workload
-    writes each sequence's row at position L - 1)."""
+    writes each sequence's row at position L - 1).  shared_blocks: pass the
+    PA_DECODE_SHARED_BLOCKS cache hint to the decode."""
     dt = torch_dtype(w)
     k, v = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim, dt,
                              device, fill=float("nan"))
@@ -69,12 +71,12 @@ def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False, ap
                                     w.max_context_len, partition_size, device)
             out = torch.empty_like(q)
             pa.append_decode_partials(q, nk, nv, k, v, bt, cl, w.max_context_len, w.scale,
-                                      partition_size, ws, out)
+                                      partition_size, ws, out, shared_blocks=shared_blocks)
             pa.decode_merge(out, cl, w.num_kv_heads, w.block_size, w.max_blocks_per_seq,
                             w.max_context_len, partition_size, ws)
         else:
             out = pa.append_decode(q, nk, nv, k, v, bt, cl, w.max_context_len, w.scale,
-                                   partition_size=partition_size)
+                                   partition_size=partition_size, shared_blocks=shared_blocks)
         torch.cuda.synchronize()
         r = {"out": out, "hist_slots": hist_slots, "new_slots": new_slots, "bt": bt, "cl": cl}
         if keep:
@@ -85,12 +87,13 @@ def run_step(w, partition_size=0, device="cuda", keep=False, two_phase=False, ap
         ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim,
                                 w.max_context_len, partition_size, device)
         out = torch.empty_like(q)
-        pa.decode_partials(q, k, v, bt, cl, w.max_context_len, w.scale, partition_size, ws, out)
+        pa.decode_partials(q, k, v, bt, cl, w.max_context_len, w.scale, partition_size, ws, out,
+                           shared_blocks=shared_blocks)
         pa.decode_merge(out, cl, w.num_kv_heads, w.block_size, w.max_blocks_per_seq,
                         w.max_context_len, partition_size, ws)
     else:
         out = pa.decode(q, k, v, bt, cl, w.max_context_len, w.scale,
-                        partition_size=partition_size)
+                        partition_size=partition_size, shared_blocks=shared_blocks)
     torch.cuda.synchronize()
     r = {"out": out, "hist_slots": hist_slots, "new_slots": new_slots, "bt": bt, "cl": cl}
     if keep:

@@ -51,12 +51,13 @@ def test_status_strings(lib):
 
 def decode_call(lib, fn="pa_decode", **kw):
     args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=4, Hq=32, Hkv=8, D=128,
-                B=16, NB=100, MB=64, maxlen=1024, scale=0.088, P=0, ws=None, wsb=0, dtype=BF16)
+                B=16, NB=100, MB=64, maxlen=1024, scale=0.088, P=0, ws=None, wsb=0, dtype=BF16,
+                flags=0)
     args.update(kw)
     a = args
     return getattr(lib, fn)(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"], a["Hq"],
                             a["Hkv"], a["D"], a["B"], a["NB"], a["MB"], a["maxlen"], a["scale"],
-                            a["P"], a["ws"], a["wsb"], a["dtype"], None)
+                            a["P"], a["ws"], a["wsb"], a["dtype"], a["flags"], None)
 
 
 @pytest.mark.parametrize("fn", ["pa_decode", "pa_decode_partials"])
@@ -78,7 +79,10 @@ def decode_call(lib, fn="pa_decode", **kw):
     (dict(P=512), WORKSPACE),                 # split without a workspace
     (dict(P=512, ws=FAKE, wsb=1000), WORKSPACE),
     (dict(P=512, ws=FAKE_MISALIGNED, wsb=1 << 30), WORKSPACE),
+    (dict(flags=2), INVALID),                 # unknown flag bit
+    (dict(flags=-1), INVALID),
     (dict(S=0), OK),                          # nothing to do: no launch
+    (dict(S=0, flags=1), OK),                 # PA_DECODE_SHARED_BLOCKS
     (dict(S=0, out=None, q=None), OK),
     # split schedule: sequences x 16-token tiles must fit in 31 bits
     (dict(S=1 << 20, MB=4096, maxlen=1 << 16, P=512, ws=FAKE, wsb=1 << 40), UNSUPPORTED),
@@ -139,12 +143,13 @@ def test_workspace_size_formula(lib):
 def append_call(lib, fn="pa_append_decode", **kw):
     args = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=4,
                 Hq=32, Hkv=8, D=128, B=16, NB=100, MB=64, maxlen=1024, scale=0.088, P=0, ws=None,
-                wsb=0, dtype=BF16)
+                wsb=0, dtype=BF16, flags=0)
     args.update(kw)
     a = args
     return getattr(lib, fn)(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["bt"],
                             a["cl"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["MB"],
-                            a["maxlen"], a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"], None)
+                            a["maxlen"], a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"],
+                            a["flags"], None)
 
 
 @pytest.mark.parametrize("fn", ["pa_append_decode", "pa_append_decode_partials"])
@@ -155,6 +160,7 @@ def append_call(lib, fn="pa_append_decode", **kw):
     (dict(Hq=30, Hkv=8), INVALID),
     (dict(D=96), UNSUPPORTED),
     (dict(P=512), WORKSPACE),
+    (dict(flags=4), INVALID),
     (dict(S=0), OK),
     (dict(S=0, key=None, value=None), OK),
 ])

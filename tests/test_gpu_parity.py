@@ -23,13 +23,14 @@ def _say(msg):
 
 
 def _check_step(w, partition_size, seqs=None, kv_heads=None, check_pool=True, two_phase=False,
-                ref=None, append=False):
+                ref=None, append=False, shared_blocks=False):
     _say(f"{w.name} S={w.num_seqs} Hq={w.num_heads} Hkv={w.num_kv_heads} D={w.head_dim} "
          f"B={w.block_size} {w.dtype} P={partition_size}" + (" two-phase" if two_phase else "")
-         + (" append" if append else ""))
+         + (" append" if append else "") + (" shared-blocks" if shared_blocks else ""))
     if ref is None:
         ref = oracle.run_step(w, seqs=seqs, kv_heads=kv_heads)
-    r = run_step(w, partition_size, keep=True, two_phase=two_phase, append=append)
+    r = run_step(w, partition_size, keep=True, two_phase=two_phase, append=append,
+                 shared_blocks=shared_blocks)
     assert np.array_equal(bits(r["hist_slots"]), ref["hist_slots"])
     assert np.array_equal(bits(r["new_slots"]), ref["new_slots"])
     if check_pool:
@@ -220,6 +221,27 @@ def test_side_stream_and_repeat_are_bit_identical():
     assert np.max(np.abs(as_f64(base) - ref)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("shape", [(8, 2, 64, 8), (32, 8, 128, 16), (16, 4, 128, 32),
+                                   (8, 1, 256, 16)])
+def test_cache_policies_give_identical_bits(shape):
+    """PA_DECODE_SHARED_BLOCKS changes only the cache bits of the K/V loads:
+    outputs and pools are bit-identical to the streaming policy's, in single
+    pass, split, two-phase and appending launches."""
+    Hq, Hkv, D, B = shape
+    w = W.custom([1, 16, 17, 200, 700, 1500], Hq, Hkv, D, B, "bf16", seed=307_045 + D + B)
+    ref = oracle.run_step(w)["out"]
+    for P, two_phase, append in ((0, False, False), (64, False, False), (512, True, False),
+                                 (0, False, True), (256, True, True)):
+        _say(f"cache policies Hq={Hq} Hkv={Hkv} D={D} B={B} P={P} two_phase={two_phase} "
+             f"append={append}")
+        a = run_step(w, P, keep=True, two_phase=two_phase, append=append, shared_blocks=False)
+        b = run_step(w, P, keep=True, two_phase=two_phase, append=append, shared_blocks=True)
+        assert np.array_equal(bits(a["out"]), bits(b["out"]))
+        assert torch.equal(a["k"].view(torch.int16), b["k"].view(torch.int16))
+        assert torch.equal(a["v"].view(torch.int16), b["v"].view(torch.int16))
+        assert np.max(np.abs(as_f64(a["out"]) - ref)) <= TOL["bf16"]
+
+
 def test_single_token_is_exact_copy():
     """L = 1: the output is the token's V row, bit for bit after rounding."""
     w = W.custom([1, 1, 1], 8, 4, 128, 16, "bf16", seed=307_051)
@@ -313,7 +335,7 @@ def test_full_shared_prefix(phase):
     w = W.shared_prefix(phase)
     ref = oracle.run_step(w)
     _check_step(w, 512, ref=ref)
-    _check_step(w, 4096, ref=ref, append=True)
+    _check_step(w, 4096, ref=ref, append=True, shared_blocks=True)
 
 
 def test_full_mixed_lengths_block_sweep():
