@@ -89,10 +89,10 @@ enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
  *   have not diverged; the pages' copy-on-write sharing).  The bf16 kernel
  *   then reads K/V with the default cache policy, so that repeated reads of a
  *   shared block can hit in the L2 or the last-level cache.  Without the flag
- *   it reads K/V tiles as streamed, read-once data (the nontemporal policy),
- *   which is faster when every block is read once per launch and slower when
- *   blocks are shared.  Results are identical either way; the fp32 kernel
- *   ignores the flag.
+ *   it reads K/V tiles as streamed, read-once data (the nontemporal policy;
+ *   block sizes 8 and 16), which is faster when every block is read once per
+ *   launch and slower when blocks are shared.  Results are identical either
+ *   way; the fp32 kernel ignores the flag.
  */
 enum { PA_DECODE_SHARED_BLOCKS = 1 };
 

@@ -32,6 +32,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
 
 
+# Per-source flags.  The decode kernel keeps its matrix-core accumulators in
+# ordinary vector registers: left to itself the compiler moves them to the
+# accumulation registers once the partition-record staging adds register
+# pressure, and then copies them back and forth around every softmax rescale.
+SOURCE_FLAGS = {
+    "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def compile_flags() -> list:
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -57,7 +66,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        jobs.append((obj, [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]))
+        jobs.append((obj, [cc, *compile_flags(), *SOURCE_FLAGS.get(src, []), "-c",
+                           os.path.join(CSRC, src), "-o", obj]))
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):

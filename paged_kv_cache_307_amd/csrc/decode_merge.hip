@@ -9,8 +9,8 @@
 // launch carry its epoch stamp.  Pairs written whole by one worker are left
 // alone; pairs of length 0 get zeros.
 //
-// One workgroup of one or four waves per (sequence, query head).  In each
-// wave, lane t handles the 16-byte dim chunk t % (D/4) of every
+// One workgroup of one, four or sixteen waves per (sequence, query head).
+// In each wave, lane t handles the 16-byte dim chunk t % (D/4) of every
 // (256/D)-th record, so each load is a coalesced float4; the lane groups'
 // partial sums meet through lane shuffles, and the waves' through LDS.
 
@@ -73,7 +73,7 @@ __device__ __forceinline__ void fold_into(Fold<CPL>& a, const Fold<CPL>& b) {
 }
 
 // NW waves per (sequence, query head): one wave for pairs with few records,
-// four when partitions are many.
+// more when partitions are many.
 template <typename Elem, int D, int NW>
 __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int B) {
   constexpr int CH = D / 4 < kThreads ? D / 4 : kThreads;  // float4 chunks per lane group
@@ -187,12 +187,17 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
 }
 
 // Waves per (sequence, query head) in the merge: one while a pair's records
-// fit in a couple of rounds of loads, four for long runs of partitions.
+// fit in a couple of rounds of loads, four for longer runs of partitions,
+// sixteen for very long ones (a 128K-token context has 256 partitions of
+// 512 tokens), so that each wave folds only a few rounds of records.
 constexpr int kWideMergeParts = 8;
+constexpr int kWiderMergeParts = 32;
 
 template <typename Elem, int D>
 hipError_t launch_merge_d(const DecodeArgs& a, int block_size, hipStream_t stream) {
   const dim3 grid(unsigned(int64_t(a.num_seqs) * a.num_heads));
+  if (a.max_partitions > kWiderMergeParts)
+    return launch(merge_kernel<Elem, D, 16>, grid, dim3(16 * kThreads), 0, stream, a, block_size);
   if (a.max_partitions > kWideMergeParts)
     return launch(merge_kernel<Elem, D, 4>, grid, dim3(4 * kThreads), 0, stream, a, block_size);
   return launch(merge_kernel<Elem, D, 1>, grid, dim3(kThreads), 0, stream, a, block_size);

@@ -36,12 +36,13 @@
 // updated running maximum: the accumulator is rescaled only when a tile's
 // maximum exceeds the maximum in use by more than 8 (a factor 256), which
 // keeps every weight <= 2^8 and is exact because the final division uses the
-// same maximum.  A piece's block-table entries are staged 64 at a time in a
+// same maximum.  A run's block-table entries are staged 64 at a time in a
 // vector register (one load per window, the next window loaded a window
 // ahead); a tile's entry is read from it into a scalar register.  K/V
 // addresses are a scalar 64-bit tile base plus a per-lane 32-bit offset, so
 // no vector ALU is spent on address arithmetic.
-// The next tile's loads are issued before the current tile is consumed.
+// The next tile's loads are issued before the current tile is consumed, also
+// across partition ends, where a split run writes a record and goes on.
 
 #include <math.h>
 
@@ -123,13 +124,12 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // ~6.4 TB/s.  When blocks are shared between sequences the default policy
 // keeps them in the caches for their other readers.  With B = 32 a 16-token
 // V tile covers half of each 128-byte line and the next tile reads the other
-// half, so V stays on the default policy there.
+// half from the L2; streaming V there costs more than it saves, and
+// streaming K alone measured slower than the default policy for both.
 constexpr int kStreamOnce = 2;
 
-template <bool kStream>
-constexpr int k_policy() { return kStream ? kStreamOnce : 0; }
 template <int B, bool kStream>
-constexpr int v_policy() { return kStream && B <= 16 ? kStreamOnce : 0; }
+constexpr int tile_policy() { return kStream && B <= 16 ? kStreamOnce : 0; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const char* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRawBufferWord3);
@@ -156,11 +156,11 @@ __device__ __forceinline__ void load_tile(Tile<D>& r, const DecodeArgs& a, const
 #pragma unroll
     for (int j = 0; j < D / 32; ++j)
       r.k[j] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * j, k_policy<kStream>()));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * j, tile_policy<B, kStream>()));
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       r.v[c] = __builtin_bit_cast(
-          uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 32 * B * c, v_policy<B, kStream>()));
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 32 * B * c, tile_policy<B, kStream>()));
     r.bad = bad;
   } else {
     const bool bad0 = unsigned(id.pb0) >= unsigned(a.num_blocks);
@@ -296,9 +296,11 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewRow<
   }
 }
 
-template <int D, int B, bool kSplit, bool kStream>
+// kParts: some pair has more than one partition, so a run may pass
+// partition ends and stage records (split launches only).
+template <int D, int B, bool kSplit, bool kStream, bool kParts>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(D > 128 || kParts ? 1 : 2)))
 void decode_bf16_mfma_kernel(DecodeArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int DCH = D / 16;
@@ -308,13 +310,24 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   const int grp = lane >> 4;
   uint16_t* out = static_cast<uint16_t*>(a.out);
   __shared__ uint32_t new_row_lds[D];  // appending decode: the new K row, then the V row
+  // Split runs stage their partition records here and store them in one
+  // burst: 32 KiB, 15 records at G = 4, D = 128 (a 128K-token context in
+  // 512-token partitions puts ~14 partitions in a worker's slice) and at
+  // least one at G = 16, D = 256.  A drain in mid-run stalls the worker's
+  // loads for several loaded round trips, so the area is sized to make it
+  // rare; four such workgroups fit on a compute unit, one per SIMD, which is
+  // as many as the decode runs.
+  constexpr int kRecLdsFloats = kParts ? 8192 : 4;
+  __shared__ __align__(16) float rec_lds[kRecLdsFloats];
 
   // Per-lane byte offsets inside a tile.
   const uint32_t k_off = uint32_t(col) * D * 2 + uint32_t(grp) * 16;
   const uint32_t v_off = uint32_t(col) * B * 2 + uint32_t(grp) * 8;
 
-  // One piece: tiles [tin, tin + ntile) of pair (s, kvh).
-  auto piece = [&](int s, int kvh, int L, int tin, int ntile, bool whole, int64_t rec_index) {
+  // One run: tiles [tin, tin + ntile) of pair (s, kvh).  The tiles of the
+  // pair's partition p go to record rec_base + p, or, when the run is the
+  // whole pair (one partition), straight to the output.
+  auto run = [&](int s, int kvh, int L, int tin, int ntile, bool whole, int64_t rec_base) {
     // Every argument is the same in all lanes; say so, so that addresses
     // built from them stay in scalar registers.
     s = wave_uniform(s);
@@ -323,13 +336,13 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     tin = wave_uniform(tin);
     ntile = wave_uniform(ntile);
     whole = wave_uniform(int(whole)) != 0;
-    rec_index = wave_uniform64(rec_index);
+    rec_base = wave_uniform64(rec_base);
     const int t_begin = tin * kTile;
     const int t_end = min(L, (tin + ntile) * kTile);
     const int nblk = (L + B - 1) / B;
     const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
 
-    // Appending decode: the piece holding the pair's last tile writes the
+    // Appending decode: the run holding the pair's last tile writes the
     // step's row (token L - 1) to its slot and uses it in that tile.
     const bool append = a.new_k != nullptr && tin + ntile == (L + kTile - 1) / kTile;
     NewRow<D> nr{};
@@ -357,6 +370,95 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
     float l_run = 0.f;
+
+    // Partition bookkeeping: the run passes partition ends without draining
+    // its loads; at each one the partition's state becomes a record and the
+    // state starts afresh.  The records wait in LDS and go to the workspace
+    // together when the run ends or the staging area is full: a global store
+    // in the loop would hold up the next tile, because the wait for a load
+    // also waits for every store issued before it.  A run's records have
+    // consecutive indices, so the burst is one linear copy.  (Without kParts
+    // every pair is a single partition and no end is passed.)
+    const int tpp = a.partition_size / kTile;
+    int part = kParts ? tin / tpp : 0;
+    int part_left = (part + 1) * tpp - tin;  // tiles of partition `part` still to consume
+    const int rec_f = int(record_floats(G, D));
+    const int slots = kRecLdsFloats / rec_f;
+    int staged = 0;  // records of partitions part - staged .. part - 1 in LDS
+
+    // The state's record layout: o[col][dims], m[col], l[col], the stamp.
+    // l is summed over the four row groups of each column first, so every
+    // lane of a column holds its (m, l).
+    auto record_to_lds = [&](int slot) {
+      const float l_tot = colsum4(l_run);
+      if (col < G) {
+        const int base = slot * rec_f;
+#pragma unroll
+        for (int c = 0; c < DCH; ++c)
+          *reinterpret_cast<floatx4_t*>(&rec_lds[base + col * D + 16 * c + 4 * grp]) = acc[c];
+        if (grp == 0) {
+          rec_lds[base + G * D + col] = m_run;
+          rec_lds[base + G * D + G + col] = l_tot;
+          if (col == 0) rec_lds[base + G * D + 2 * G] = __uint_as_float(a.epoch);
+        }
+      }
+    };
+    auto record_to_workspace = [&](int p) {
+      const float l_tot = colsum4(l_run);
+      if (col < G) {
+        float* rec = a.ws + (rec_base + p) * rec_f;
+#pragma unroll
+        for (int c = 0; c < DCH; ++c)
+          *reinterpret_cast<floatx4_t*>(rec + col * D + 16 * c + 4 * grp) = acc[c];
+        if (grp == 0) {
+          rec[G * D + col] = m_run;
+          rec[G * D + G + col] = l_tot;
+          if (col == 0) rec[G * D + 2 * G] = __uint_as_float(a.epoch);
+        }
+      }
+    };
+    // Copies n staged records, partitions p_first .., to the workspace,
+    // eight 16-byte chunks per lane in flight at a time.
+    auto drain = [&](int p_first, int n) {
+      __syncthreads();  // one wave: orders the LDS writes before the reads
+      const floatx4_t* src = reinterpret_cast<const floatx4_t*>(rec_lds);
+      floatx4_t* dst = reinterpret_cast<floatx4_t*>(a.ws + (rec_base + p_first) * rec_f);
+      const int n4 = n * rec_f / 4;
+      constexpr int kBurst = 8;
+      for (int i0 = 0; i0 < n4; i0 += kBurst * kThreads) {
+        floatx4_t v[kBurst];
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          const int i = i0 + u * kThreads + lane;
+          if (i < n4) v[u] = src[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          const int i = i0 + u * kThreads + lane;
+          if (i < n4) dst[i] = v[u];
+        }
+      }
+      __syncthreads();  // and the reads before the slots are written again
+    };
+    // The run's end: the output itself for a whole pair, else the staged
+    // records and the last partition's (stored directly: the run is over).
+    auto finish = [&]() {
+      if (whole) {
+        const float l_tot = colsum4(l_run);
+        if (col < G) {
+          const float inv_l = 1.0f / l_tot;
+          uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G + col) * D + 4 * grp;
+#pragma unroll
+          for (int c = 0; c < DCH; ++c)
+            *reinterpret_cast<uint2*>(o + 16 * c) =
+                make_uint2(pack_bf16x2_rne(acc[c][0] * inv_l, acc[c][1] * inv_l),
+                           pack_bf16x2_rne(acc[c][2] * inv_l, acc[c][3] * inv_l));
+        }
+      } else {
+        if (staged > 0) drain(part - staged, staged);
+        record_to_workspace(part);
+      }
+    };
 
     auto t0_of = [&](int k) { return t_begin + k * kTile; };
 
@@ -408,7 +510,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                                                            pop, acc[c], 0, 0, 0);
     };
 
-    // Software pipeline over the piece's tiles, a ring of kRing register
+    // Software pipeline over the run's tiles, a ring of kRing register
     // tiles: while tile k is consumed, tiles k+1 .. k+kRing-1 are in flight.
     // Every load is issued unconditionally (past the last tile the ring
     // repeats the last tile, which the caches serve) and only the consumes
@@ -451,6 +553,20 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
               if (append && k + d == ntile - 1)
                 put_new_row<D>(ring[d], new_row_lds, t_end - 1 - t0_of(k + d), col, grp);
               consume(ring[d], k + d);
+              if (kParts && --part_left == 0 && k + d + 1 < ntile) {
+                record_to_lds(staged);
+                ++staged;
+                ++part;
+                part_left = tpp;
+#pragma unroll
+                for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                m_run = -INFINITY;
+                l_run = 0.f;
+                if (staged == slots) {
+                  drain(part - staged, staged);
+                  staged = 0;
+                }
+              }
             }
           }
         }
@@ -458,34 +574,11 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // l over the four row groups of each column; every lane of a column
-    // then holds the column's (m, l).
-    const float l_tot = colsum4(l_run);
-    if (col < G) {
-      if (whole) {
-        const float inv_l = 1.0f / l_tot;
-        uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G + col) * D + 4 * grp;
-#pragma unroll
-        for (int c = 0; c < DCH; ++c)
-          *reinterpret_cast<uint2*>(o + 16 * c) =
-              make_uint2(pack_bf16x2_rne(acc[c][0] * inv_l, acc[c][1] * inv_l),
-                         pack_bf16x2_rne(acc[c][2] * inv_l, acc[c][3] * inv_l));
-      } else {
-        float* rec = a.ws + rec_index * record_floats(G, D);
-#pragma unroll
-        for (int c = 0; c < DCH; ++c)
-          *reinterpret_cast<floatx4_t*>(rec + col * D + 16 * c + 4 * grp) = acc[c];
-        if (grp == 0) {
-          rec[G * D + col] = m_run;
-          rec[G * D + G + col] = l_tot;
-          if (col == 0) rec[G * D + 2 * G] = __uint_as_float(a.epoch);
-        }
-      }
-    }
+    finish();
   };
 
   if constexpr (kSplit) {
-    walk_slice(a, B, lane, blockIdx.x, piece);
+    walk_slice_runs(a, B, lane, blockIdx.x, run);
   } else {
     // one worker per (sequence, KV head); consecutive workers are the KV
     // heads of one sequence (workgroup i runs on XCD i % 8)
@@ -497,17 +590,20 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       for (int i = lane; i < G * D; i += kThreads) o[i] = 0;
       return;
     }
-    piece(s, kvh, L, 0, (L + kTile - 1) / kTile, true, 0);
+    run(s, kvh, L, 0, (L + kTile - 1) / kTile, true, 0);
   }
 }
 
 template <int D, int B, bool kStream>
 hipError_t launch_policy(const DecodeArgs& a, hipStream_t stream) {
+  if (a.split && a.max_partitions > 1)
+    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, true>, dim3(unsigned(a.workers)),
+                  dim3(kThreads), 0, stream, a);
   if (a.split)
-    return launch(decode_bf16_mfma_kernel<D, B, true, kStream>, dim3(unsigned(a.workers)),
+    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, false>, dim3(unsigned(a.workers)),
                   dim3(kThreads), 0, stream, a);
   const int64_t grid = int64_t(a.num_seqs) * a.num_kv_heads;
-  return launch(decode_bf16_mfma_kernel<D, B, false, kStream>, dim3(unsigned(grid)),
+  return launch(decode_bf16_mfma_kernel<D, B, false, kStream, false>, dim3(unsigned(grid)),
                 dim3(kThreads), 0, stream, a);
 }
 
@@ -517,13 +613,14 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
                          : launch_policy<D, B, true>(a, stream);
 }
 
-// The worker count of both cache policies is the streaming variant's:
-// pa_decode_merge, which is not told the policy, rebuilds the same schedule
-// from it.  (The two variants differ only in a load's cache bits.)
+// One worker count for every split variant: pa_decode_merge, which is not
+// told the cache policy, rebuilds the same schedule from it.  It is taken
+// from the variant that stages records (the one using the most LDS), so
+// every variant fits that many workers on the device at once.
 template <int D, int B>
 int workers_one() {
   return resident_workers(
-      reinterpret_cast<const void*>(decode_bf16_mfma_kernel<D, B, true, true>), kThreads);
+      reinterpret_cast<const void*>(decode_bf16_mfma_kernel<D, B, true, true, true>), kThreads);
 }
 
 template <int D>

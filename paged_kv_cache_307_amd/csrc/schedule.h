@@ -17,6 +17,8 @@
 // cut raises gp or b (or both), so indices are distinct and below
 // total_partitions + W.  A piece that is a whole pair writes the final
 // output instead of a record.  The merge walks the same cuts per pair.
+// (A worker may stream one pair's pieces back to back as a single run,
+// writing each partition's record as it passes the partition's end.)
 #pragma once
 
 #include "device_common.h"
@@ -137,15 +139,19 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
   return r;
 }
 
-// Calls piece(s, g, L, first_tile, num_tiles, whole, record_index) for
-// every piece of worker b's slice, in line order.
-template <typename PieceFn>
-__device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, int lane, int b,
-                                           PieceFn&& piece) {
+// Calls run(s, g, L, first_tile, num_tiles, whole, rec_base) for every run
+// of consecutive tiles of one pair in worker b's slice, in line order.  A
+// run ends only at a pair boundary or at the slice's end; it may span
+// several partitions, and the tiles of the pair's partition p (p = tile *
+// 16 / partition_size) belong to the record at index rec_base + p.  whole:
+// the run is the entire pair and the pair has one partition, so the output
+// is written directly and no record is made.
+template <typename RunFn>
+__device__ __forceinline__ void walk_slice_runs(const DecodeArgs& a, int block_size, int lane,
+                                                int b, RunFn&& run) {
   const Slice sl = locate_slice(a, block_size, lane, b);
   if (sl.x0 >= sl.x1) return;
   const int Hkv = a.num_kv_heads;
-  const int tpp = a.partition_size / 16;  // tiles per partition
   int s = sl.seq;
   int64_t sbase = sl.pref_t * Hkv;        // line start of sequence s
   int64_t gpb = sl.pref_p * Hkv;          // first partition index of sequence s
@@ -168,16 +174,35 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, 
     const int64_t off = cur - sbase;
     const int g = int(off / ps.tiles);
     const int tin = int(off - int64_t(g) * ps.tiles);
-    const int part = tin / tpp;
-    int64_t end = sbase + int64_t(g + 1) * ps.tiles;
-    end = min(end, sbase + int64_t(g) * ps.tiles + int64_t(part + 1) * tpp);
-    end = min(end, sl.x1);
+    const int64_t end = min(sbase + int64_t(g + 1) * ps.tiles, sl.x1);
     const int ntile = int(end - cur);
-    const bool whole = tin == 0 && ntile == ps.tiles;
-    const int64_t rec = gpb + int64_t(g) * ps.parts + part + b;
-    piece(s, g, len, tin, ntile, whole, rec);
+    const bool whole = tin == 0 && ntile == ps.tiles && ps.parts == 1;
+    run(s, g, len, tin, ntile, whole, gpb + int64_t(g) * ps.parts + b);
     cur = end;
   }
+}
+
+// Calls piece(s, g, L, first_tile, num_tiles, whole, record_index) for
+// every piece of worker b's slice, in line order: the runs above, cut
+// further at partition boundaries.
+template <typename PieceFn>
+__device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, int lane, int b,
+                                           PieceFn&& piece) {
+  const int tpp = a.partition_size / 16;  // tiles per partition
+  walk_slice_runs(a, block_size, lane, b,
+                  [&](int s, int g, int len, int tin, int ntile, bool whole, int64_t rec_base) {
+                    if (whole) {
+                      piece(s, g, len, tin, ntile, true, rec_base);
+                      return;
+                    }
+                    const int end = tin + ntile;
+                    for (int t = tin; t < end;) {
+                      const int part = t / tpp;
+                      const int e = min(end, (part + 1) * tpp);
+                      piece(s, g, len, t, e - t, false, rec_base + part);
+                      t = e;
+                    }
+                  });
 }
 
 // Record indices of pair (s, g): every piece of the pair has an index in

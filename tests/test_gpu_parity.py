@@ -242,6 +242,28 @@ def test_cache_policies_give_identical_bits(shape):
         assert np.max(np.abs(as_f64(a["out"]) - ref)) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("shape", [
+    # (lengths, Hq, Hkv, D): G = 16 at D = 128 stages 3 records per run, G = 16
+    # at D = 256 one; G = 4 at D = 128 stages 15, and 20000-token pairs in
+    # 16-token partitions give runs of ~28 partitions
+    ([6000, 7000, 5000, 30], 32, 2, 128),
+    ([6000, 7000, 5000, 30], 16, 1, 256),
+    ([20000, 20000, 3000, 17], 32, 8, 128),
+])
+def test_partition_records_staged_and_drained(shape):
+    """Split runs that pass many partition ends stage the partitions'
+    records in LDS and store them in bursts, also in mid-run when the
+    staging area fills; every record must reach the merge."""
+    lengths, Hq, Hkv, D = shape
+    w = W.custom(lengths, Hq, Hkv, D, 16, "bf16", seed=307_046 + Hq + D)
+    ref = oracle.run_step(w, seqs=range(w.num_seqs), kv_heads=[0, Hkv - 1])
+    for P in (16, 32):
+        _check_step(w, P, seqs=range(w.num_seqs), kv_heads=[0, Hkv - 1], check_pool=False,
+                    ref=ref)
+    _check_step(w, 16, seqs=range(w.num_seqs), kv_heads=[0, Hkv - 1], check_pool=False, ref=ref,
+                append=True, two_phase=True)
+
+
 def test_single_token_is_exact_copy():
     """L = 1: the output is the token's V row, bit for bit after rounding."""
     w = W.custom([1, 1, 1], 8, 4, 128, 16, "bf16", seed=307_051)
