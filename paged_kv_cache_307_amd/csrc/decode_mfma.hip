@@ -297,10 +297,10 @@ __device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewRow<
 }
 
 // kParts: some pair has more than one partition, so a run may pass
-// partition ends and stage records (split launches only).
+// partition ends (split launches only).
 template <int D, int B, bool kSplit, bool kStream, bool kParts>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D > 128 || kParts ? 1 : 2)))
+__attribute__((amdgpu_waves_per_eu(D > 128 || kSplit ? 1 : 2)))
 void decode_bf16_mfma_kernel(DecodeArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int DCH = D / 16;
@@ -310,15 +310,49 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   const int grp = lane >> 4;
   uint16_t* out = static_cast<uint16_t*>(a.out);
   __shared__ uint32_t new_row_lds[D];  // appending decode: the new K row, then the V row
-  // Split runs stage their partition records here and store them in one
-  // burst: 32 KiB, 15 records at G = 4, D = 128 (a 128K-token context in
-  // 512-token partitions puts ~14 partitions in a worker's slice) and at
-  // least one at G = 16, D = 256.  A drain in mid-run stalls the worker's
-  // loads for several loaded round trips, so the area is sized to make it
-  // rare; four such workgroups fit on a compute unit, one per SIMD, which is
-  // as many as the decode runs.
-  constexpr int kRecLdsFloats = kParts ? 8192 : 4;
+  // A split worker's records wait here, with their workspace indices, and
+  // go out in bursts: when the area is full and after the worker's last
+  // run.  A global store in mid-stream would hold up the worker's next
+  // loads, because the wait for a load also waits for every store issued
+  // before it; a store's acknowledgement under full load takes a long
+  // round trip.  32 KiB holds 15 records at G = 4, D = 128 (a 128K-token
+  // context in 512-token partitions puts ~14 partitions in a worker's
+  // slice) and at least one at G = 16, D = 256.  Four such workgroups fit
+  // on a compute unit, one per SIMD, as many as the decode runs.
+  constexpr int kRecLdsFloats = kSplit ? 8192 : 4;
+  constexpr int kMaxStaged = kSplit ? 16 : 1;
   __shared__ __align__(16) float rec_lds[kRecLdsFloats];
+  __shared__ int64_t rec_dst[kMaxStaged];
+  const int rec_f = int(record_floats(G, D));
+  const int slots = min(kMaxStaged, kRecLdsFloats / rec_f);
+  int staged = 0;  // records waiting in LDS
+
+  // Copies the staged records to their places in the workspace, eight
+  // 16-byte chunks per lane in flight at a time.
+  auto drain = [&]() {
+    __syncthreads();  // one wave: orders the LDS writes before the reads
+    const int q4 = rec_f / 4;
+    constexpr int kBurst = 8;
+    for (int sl = 0; sl < staged; ++sl) {
+      const floatx4_t* src = reinterpret_cast<const floatx4_t*>(rec_lds + sl * rec_f);
+      floatx4_t* dst = reinterpret_cast<floatx4_t*>(a.ws + wave_uniform64(rec_dst[sl]) * rec_f);
+      for (int i0 = 0; i0 < q4; i0 += kBurst * kThreads) {
+        floatx4_t v[kBurst];
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          const int i = i0 + u * kThreads + lane;
+          if (i < q4) v[u] = src[i];
+        }
+#pragma unroll
+        for (int u = 0; u < kBurst; ++u) {
+          const int i = i0 + u * kThreads + lane;
+          if (i < q4) dst[i] = v[u];
+        }
+      }
+    }
+    __syncthreads();  // and the reads before the slots are written again
+    staged = 0;
+  };
 
   // Per-lane byte offsets inside a tile.
   const uint32_t k_off = uint32_t(col) * D * 2 + uint32_t(grp) * 16;
@@ -372,27 +406,20 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     float l_run = 0.f;
 
     // Partition bookkeeping: the run passes partition ends without draining
-    // its loads; at each one the partition's state becomes a record and the
-    // state starts afresh.  The records wait in LDS and go to the workspace
-    // together when the run ends or the staging area is full: a global store
-    // in the loop would hold up the next tile, because the wait for a load
-    // also waits for every store issued before it.  A run's records have
-    // consecutive indices, so the burst is one linear copy.  (Without kParts
+    // its loads; at each one the partition's state becomes a record (staged
+    // like every record) and the state starts afresh.  (Without kParts
     // every pair is a single partition and no end is passed.)
     const int tpp = a.partition_size / kTile;
     int part = kParts ? tin / tpp : 0;
     int part_left = (part + 1) * tpp - tin;  // tiles of partition `part` still to consume
-    const int rec_f = int(record_floats(G, D));
-    const int slots = kRecLdsFloats / rec_f;
-    int staged = 0;  // records of partitions part - staged .. part - 1 in LDS
 
-    // The state's record layout: o[col][dims], m[col], l[col], the stamp.
-    // l is summed over the four row groups of each column first, so every
-    // lane of a column holds its (m, l).
-    auto record_to_lds = [&](int slot) {
+    // Stages the state as the record of partition p: o[col][dims], m[col],
+    // l[col], the stamp.  l is summed over the four row groups of each
+    // column first, so every lane of a column holds its (m, l).
+    auto stage = [&](int p) {
       const float l_tot = colsum4(l_run);
       if (col < G) {
-        const int base = slot * rec_f;
+        const int base = staged * rec_f;
 #pragma unroll
         for (int c = 0; c < DCH; ++c)
           *reinterpret_cast<floatx4_t*>(&rec_lds[base + col * D + 16 * c + 4 * grp]) = acc[c];
@@ -402,46 +429,11 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
           if (col == 0) rec_lds[base + G * D + 2 * G] = __uint_as_float(a.epoch);
         }
       }
+      if (lane == 0) rec_dst[staged] = rec_base + p;
+      if (++staged == slots) drain();
     };
-    auto record_to_workspace = [&](int p) {
-      const float l_tot = colsum4(l_run);
-      if (col < G) {
-        float* rec = a.ws + (rec_base + p) * rec_f;
-#pragma unroll
-        for (int c = 0; c < DCH; ++c)
-          *reinterpret_cast<floatx4_t*>(rec + col * D + 16 * c + 4 * grp) = acc[c];
-        if (grp == 0) {
-          rec[G * D + col] = m_run;
-          rec[G * D + G + col] = l_tot;
-          if (col == 0) rec[G * D + 2 * G] = __uint_as_float(a.epoch);
-        }
-      }
-    };
-    // Copies n staged records, partitions p_first .., to the workspace,
-    // eight 16-byte chunks per lane in flight at a time.
-    auto drain = [&](int p_first, int n) {
-      __syncthreads();  // one wave: orders the LDS writes before the reads
-      const floatx4_t* src = reinterpret_cast<const floatx4_t*>(rec_lds);
-      floatx4_t* dst = reinterpret_cast<floatx4_t*>(a.ws + (rec_base + p_first) * rec_f);
-      const int n4 = n * rec_f / 4;
-      constexpr int kBurst = 8;
-      for (int i0 = 0; i0 < n4; i0 += kBurst * kThreads) {
-        floatx4_t v[kBurst];
-#pragma unroll
-        for (int u = 0; u < kBurst; ++u) {
-          const int i = i0 + u * kThreads + lane;
-          if (i < n4) v[u] = src[i];
-        }
-#pragma unroll
-        for (int u = 0; u < kBurst; ++u) {
-          const int i = i0 + u * kThreads + lane;
-          if (i < n4) dst[i] = v[u];
-        }
-      }
-      __syncthreads();  // and the reads before the slots are written again
-    };
-    // The run's end: the output itself for a whole pair, else the staged
-    // records and the last partition's (stored directly: the run is over).
+    // The run's end: the output itself for a whole pair, else the last
+    // partition's record.
     auto finish = [&]() {
       if (whole) {
         const float l_tot = colsum4(l_run);
@@ -455,8 +447,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                            pack_bf16x2_rne(acc[c][2] * inv_l, acc[c][3] * inv_l));
         }
       } else {
-        if (staged > 0) drain(part - staged, staged);
-        record_to_workspace(part);
+        stage(part);
       }
     };
 
@@ -554,18 +545,13 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                 put_new_row<D>(ring[d], new_row_lds, t_end - 1 - t0_of(k + d), col, grp);
               consume(ring[d], k + d);
               if (kParts && --part_left == 0 && k + d + 1 < ntile) {
-                record_to_lds(staged);
-                ++staged;
+                stage(part);
                 ++part;
                 part_left = tpp;
 #pragma unroll
                 for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
                 m_run = -INFINITY;
                 l_run = 0.f;
-                if (staged == slots) {
-                  drain(part - staged, staged);
-                  staged = 0;
-                }
               }
             }
           }
@@ -579,6 +565,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
 
   if constexpr (kSplit) {
     walk_slice_runs(a, B, lane, blockIdx.x, run);
+    if (staged > 0) drain();
   } else {
     // one worker per (sequence, KV head); consecutive workers are the KV
     // heads of one sequence (workgroup i runs on XCD i % 8)
@@ -615,8 +602,8 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
 
 // One worker count for every split variant: pa_decode_merge, which is not
 // told the cache policy, rebuilds the same schedule from it.  It is taken
-// from the variant that stages records (the one using the most LDS), so
-// every variant fits that many workers on the device at once.
+// from the variant with the most registers, so every variant fits that
+// many workers on the device at once (all split variants use the same LDS).
 template <int D, int B>
 int workers_one() {
   return resident_workers(
