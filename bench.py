@@ -49,16 +49,16 @@ sys.path.insert(0, ROOT)
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
 # (FETCH_SIZE, then WRITE_SIZE) over this script's default run, each scaled by
 # what the same counter reads for pa_copy_blocks on a known byte count (run
-# with --copy-calibration): FETCH_SIZE x 1.99183, WRITE_SIZE x 1.0.  Summary
+# with --copy-calibration): FETCH_SIZE x 1.99187, WRITE_SIZE x 1.0.  Summary
 # and commands: profiles/append_decode_partials_llama3_8b_decode_hbm_bytes.md.  The
 # figure holds only for the kernel sources it was measured with.
 KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache_307_amd/csrc/schedule.h",
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
-                  "paged_kv_cache_307_amd/csrc/api.hip"]
+                  "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False): {
-        "bytes": 546613614, "fetch_bytes": 541747043, "write_bytes": 4866572,
-        "sources_sha256": "3b0120a45493730646f646ecec6741a7e8f81f504cb4a1f7014b275a9991f363"},
+        "bytes": 552518736, "fetch_bytes": 547658996, "write_bytes": 4859740,
+        "sources_sha256": "a1a7012a270d9cb014576ef13880f3266249c52a6ea3dae2c56899e08c88d48f"},
 }
 
 
@@ -210,6 +210,8 @@ def main():
     B = w.block_size
     P = default_partition if args.partition is None else args.partition
     shared = shares_blocks(w) if args.shared_blocks == "auto" else args.shared_blocks == "on"
+    # some pair spans more than one partition (selects the kernel variant)
+    multi_part = -(-min(w.max_context_len, w.max_blocks_per_seq * B) // P) > 1
     hist_bt, bt, cl = t(w.hist_block_tables), t(w.block_tables), t(w.context_lens)
     k0, v0 = pa.empty_kv_cache(w.num_blocks, w.num_kv_heads, B, w.head_dim, dt, dev,
                                fill=float("nan"))
@@ -225,19 +227,19 @@ def main():
     ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, P, dev)
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
+    def partials(i):
         k, v = layers[i % len(layers)]
-        if args.separate_write:
-            pa.write_kv(k, v, new_k, new_v, new_slots)
-        if ev is not None:
-            ev[0].record()
         if args.separate_write:
             pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out, shared_blocks=shared)
         else:
             pa.append_decode_partials(q, new_k, new_v, k, v, bt, cl, mcl, w.scale, P, ws, out,
                                       shared_blocks=shared)
-        if ev is not None:
-            ev[1].record()
+
+    def step(i):
+        if args.separate_write:
+            k, v = layers[i % len(layers)]
+            pa.write_kv(k, v, new_k, new_v, new_slots)
+        partials(i)
         pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
 
     for i in range(args.warmup):
@@ -252,23 +254,24 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    # The same K steps again with HIP events recorded on the launch stream
-    # around every launch of the dominant kernel (two event records per
-    # step add a few microseconds to each step, so this pass is kept apart
-    # from the one that gives the step time).
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The dominant kernel alone: K of its launches back to back on the
+    # launch stream, between two HIP events (an event record between
+    # launches would add a gap of its own to each).  Successive launches
+    # are independent: each reads its layer's cache and rewrites the
+    # workspace records.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    ev0.record()
     for i in range(args.steps):
-        step(i, evs[i])
+        partials(i)
+    ev1.record()
     torch.cuda.synchronize()
-    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_avg_ms = ev0.elapsed_time(ev1) / args.steps
 
     ms_per_step = elapsed * 1e3 / args.steps
     ab = algorithmic_bytes(w)
     step_bytes = sum(ab.values())
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    part_avg_ms = float(np.mean(part_ms))
     # the timed kernel: reads K/V, q, table entries and lengths; in the
     # appending step it also stores the rows (the merge writes most of out)
     part_bytes = ab["kv"] + ab["q"] + ab["table"] + ab["context_lens"]
@@ -303,7 +306,8 @@ def main():
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
         "roofline": {
-            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true,{str(not shared).lower()}> (" +
+            "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true,{str(not shared).lower()},"
+                      f"{str(multi_part).lower()}> (" +
                       ("pa_decode_partials" if args.separate_write else "pa_append_decode_partials") + ")",
             "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
