@@ -169,8 +169,11 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, i
  * where, over the piece's tokens t and with x_t = scale * log2(e) * q.k_t,
  *   m = max_t x_t,  l = sum_t 2^(x_t - m),  o = sum_t 2^(x_t - m) v_t.
  * A piece that is a whole pair writes its output directly instead.  The
- * workspace holds a small block of per-launch metadata and the records; it
- * must be 16-byte aligned and at least pa_decode_workspace_bytes() long.
+ * workspace holds a small block of per-launch metadata and room for
+ * num_seqs * num_kv_heads * (4 + ceil(max_context_len / partition_size))
+ * + 4096 records (the first four records of each pair in slots of their
+ * own, so the merge finds them without a lookup); it must be 16-byte
+ * aligned and at least pa_decode_workspace_bytes() long.
  * Allocate it zero-filled once and reuse it: each launch stamps its records,
  * so records left by earlier launches are ignored (zero is never a stamp).
  * pa_decode_workspace_bytes returns 0 when partition_size == 0 (single pass,
@@ -210,7 +213,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * included).  Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED /
  * PA_ERR_WORKSPACE on a failed check; with partition_size > 0,
  * PA_ERR_UNSUPPORTED also when num_seqs * ceil(max_context_len / 16)
- * exceeds 2^31 - 1 (the split schedule counts tiles in 32-bit integers).
+ * exceeds 2^31 - 1 or, times num_kv_heads, reaches 2^40 (the split schedule
+ * counts tiles per KV head in 32-bit integers and divides line positions in
+ * doubles).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,

@@ -87,6 +87,13 @@ int64_t effective_max_len(int32_t max_context_len, int32_t max_blocks_per_seq, i
   return max_context_len < cap ? max_context_len : cap;
 }
 
+// Sizes the split schedule handles: S * ceil(L_max / 16) tiles per KV head
+// within 31 bits, and a line of fewer than 2^40 tiles in all.
+bool split_line_fits(int32_t num_seqs, int32_t num_kv_heads, int64_t max_len) {
+  const int64_t tiles = int64_t(num_seqs) * ((max_len + 15) / 16);
+  return tiles <= 0x7FFFFFFF && tiles * num_kv_heads < (int64_t(1) << 40);
+}
+
 int64_t max_parts_for(int64_t max_len, int32_t partition_size) {
   const int64_t parts = (max_len + partition_size - 1) / partition_size;
   return parts > 1 ? parts : 1;
@@ -142,7 +149,8 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
 
   const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
   // the split schedule sums 16-token tiles over sequences in 32-bit integers
-  if (partition_size > 0 && int64_t(num_seqs) * ((max_len + 15) / 16) > 0x7FFFFFFF)
+  // and divides line positions (tiles x KV heads) times workers in doubles
+  if (partition_size > 0 && !split_line_fits(num_seqs, num_kv_heads, max_len))
     return PA_ERR_UNSUPPORTED;
   DecodeArgs& a = plan->args;
   plan->split = partition_size > 0;
@@ -318,7 +326,7 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
       int64_t(workspace_bytes) < workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts))
     return PA_ERR_WORKSPACE;
   if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-  if (int64_t(num_seqs) * ((max_len + 15) / 16) > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  if (!split_line_fits(num_seqs, num_kv_heads, max_len)) return PA_ERR_UNSUPPORTED;
   const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size);
   if (workers <= 0) return PA_ERR_HIP;
   DecodeArgs a{};

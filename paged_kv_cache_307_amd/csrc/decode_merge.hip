@@ -5,8 +5,9 @@
 // the piece's maximum of scale * log2(e) * q.k, l_p = sum of 2^(x - m_p),
 // o_p = sum of 2^(x - m_p) v), the exact softmax result is
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p l_p.
-// A pair's records lie in a short index range (schedule.h); records of this
-// launch carry its epoch stamp.  Pairs written whole by one worker are left
+// A pair's records are numbered from 0 in line order; the first few sit in
+// slots indexed by the pair, the rest in an overflow region (schedule.h).
+// Records of this launch carry its epoch stamp.  Pairs written whole by one worker are left
 // alone; pairs of length 0 get zeros.
 //
 // One workgroup of one, four or sixteen waves per (sequence, query head).
@@ -89,66 +90,92 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
   const int lane = threadIdx.x % kThreads;
   const int wave = threadIdx.x / kThreads;
   Elem* out = static_cast<Elem*>(a.out) + (int64_t(s) * a.num_heads + h) * D;
-  PairRecords pr;
-  if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
-    for (int i = threadIdx.x; i < D; i += kThreads * NW) out[i] = from_f32<Elem>(0.f);
-    return;
-  }
-  if (pr.whole) return;  // written whole by its worker
   const int64_t R = record_floats(G, D);
-  const float* base = a.ws + pr.first * R;
-  const int count = int(pr.last - pr.first + 1);
-
-  // One pass: lane (pg, c) folds records pg, pg + PG, ... into a running
-  // (max, denominator, numerator chunks c, c + CH, ...), rescaling when the
-  // max grows.  The loads of kUnroll records are issued together and
-  // unconditionally (a stamp from another launch only drops the record
-  // afterwards), so a pair costs one round trip to memory per kUnroll
-  // records per lane.
-  constexpr int kUnroll = 2;
   const int c = lane % CH;
   const int pg = wave * GPW + lane / CH;
+
+  // Lane (pg, c) folds records pg, pg + PG, ... into a running (max,
+  // denominator, numerator chunks c, c + CH, ...), rescaling when the max
+  // grows.  A stamp from another launch drops a record.
   Fold<CPL> f;
   f.m = -INFINITY;
   f.den = 0.f;
 #pragma unroll
   for (int i = 0; i < CPL; ++i) f.num[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int q0 = pg; q0 < count; q0 += PG * kUnroll) {
-    uint32_t st[kUnroll];
-    float mq[kUnroll], lq[kUnroll];
-    float4 oq[kUnroll][CPL];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float* rec = base + int64_t(min(q0 + u * PG, count - 1)) * R;
-      st[u] = __float_as_uint(rec[G * D + 2 * G]);
-      mq[u] = rec[G * D + hl];
-      lq[u] = rec[G * D + G + hl];
-#pragma unroll
-      for (int i = 0; i < CPL; ++i)
-        oq[u][i] = *reinterpret_cast<const float4*>(rec + hl * D + 4 * (c + CH * i));
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (q0 + u * PG >= count || st[u] != pr.epoch) continue;
-      if (mq[u] > f.m) {
-        const float r = exp2f(f.m - mq[u]);  // 0 on the first record
-        f.den *= r;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-          f.num[i].x *= r; f.num[i].y *= r; f.num[i].z *= r; f.num[i].w *= r;
-        }
-        f.m = mq[u];
-      }
-      const float w = exp2f(mq[u] - f.m);
-      f.den += w * lq[u];
+  auto fold_record = [&](float mq, float lq, const float4* oq) {
+    if (mq > f.m) {
+      const float r = exp2f(f.m - mq);  // 0 on the first record
+      f.den *= r;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
-        f.num[i].x += w * oq[u][i].x;
-        f.num[i].y += w * oq[u][i].y;
-        f.num[i].z += w * oq[u][i].z;
-        f.num[i].w += w * oq[u][i].w;
+        f.num[i].x *= r; f.num[i].y *= r; f.num[i].z *= r; f.num[i].w *= r;
       }
+      f.m = mq;
     }
+    const float w = exp2f(mq - f.m);
+    f.den += w * lq;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      f.num[i].x += w * oq[i].x;
+      f.num[i].y += w * oq[i].y;
+      f.num[i].z += w * oq[i].z;
+      f.num[i].w += w * oq[i].w;
+    }
+  };
+  struct Loaded {
+    uint32_t st;
+    float m, l;
+    float4 o[CPL];
+  };
+  auto load_record = [&](int64_t slot) {
+    const float* rec = a.ws + slot * R;
+    Loaded r;
+    r.st = __float_as_uint(rec[G * D + 2 * G]);
+    r.m = rec[G * D + hl];
+    r.l = rec[G * D + G + hl];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      r.o[i] = *reinterpret_cast<const float4*>(rec + hl * D + 4 * (c + CH * i));
+    return r;
+  };
+
+  // Records 0 .. kPairSlots - 1 sit in slots indexed by the pair, so their
+  // loads go out together with the meta block's, before the pair's record
+  // count is known; most pairs have no others.
+  constexpr int KF = (kPairSlots + PG - 1) / PG;  // pair slots per lane
+  const int64_t fixed0 = pair_fixed_slot(a, s, kvh);
+  Loaded fr[KF];
+#pragma unroll
+  for (int u = 0; u < KF; ++u) fr[u] = load_record(fixed0 + min(pg + u * PG, kPairSlots - 1));
+  // keep them ahead of the length and meta loads below: the compiler would
+  // otherwise sink them past the empty-sequence exit, after its wait
+  asm volatile("" ::: "memory");
+
+  PairRecords pr;
+  if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
+    for (int i = lane + wave * kThreads; i < D; i += kThreads * NW) out[i] = from_f32<Elem>(0.f);
+    return;
+  }
+  if (pr.whole) return;  // written whole by its worker
+#pragma unroll
+  for (int u = 0; u < KF; ++u) {
+    const int k = pg + u * PG;
+    if (k < kPairSlots && k < pr.count && fr[u].st == pr.epoch)
+      fold_record(fr[u].m, fr[u].l, fr[u].o);
+  }
+
+  // The rest, from the overflow region: the loads of kUnroll records are
+  // issued together and unconditionally (clamped to the last record), so a
+  // pair costs one more round trip to memory per kUnroll records per lane.
+  constexpr int kUnroll = 2;
+  for (int q0 = kPairSlots + pg; q0 < pr.count; q0 += PG * kUnroll) {
+    Loaded r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      r[u] = load_record(pr.slots.overflow + min(q0 + u * PG, pr.count - 1));
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (q0 + u * PG < pr.count && r[u].st == pr.epoch) fold_record(r[u].m, r[u].l, r[u].o);
   }
   // Fold the wave's record groups (lanes c, c + CH, ...) together through
   // lane shuffles; every lane of a chunk ends with the wave's state.

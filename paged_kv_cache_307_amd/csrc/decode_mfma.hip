@@ -324,7 +324,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   __shared__ __align__(16) float rec_lds[kRecLdsFloats];
   __shared__ int64_t rec_dst[kMaxStaged];
   const int rec_f = int(record_floats(G, D));
-  const int slots = min(kMaxStaged, kRecLdsFloats / rec_f);
+  const int stage_slots = min(kMaxStaged, kRecLdsFloats / rec_f);
   int staged = 0;  // records waiting in LDS
 
   // Copies the staged records to their places in the workspace, eight
@@ -359,9 +359,11 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   const uint32_t v_off = uint32_t(col) * B * 2 + uint32_t(grp) * 8;
 
   // One run: tiles [tin, tin + ntile) of pair (s, kvh).  The tiles of the
-  // pair's partition p go to record rec_base + p, or, when the run is the
-  // whole pair (one partition), straight to the output.
-  auto run = [&](int s, int kvh, int L, int tin, int ntile, bool whole, int64_t rec_base) {
+  // pair's partition p make its record k0 + p (stored at record_slot(slots,
+  // k0 + p)), or, when the run is the whole pair (one partition), go
+  // straight to the output.
+  auto run = [&](int s, int kvh, int L, int tin, int ntile, bool whole, PairSlots slots,
+                 int k0) {
     // Every argument is the same in all lanes; say so, so that addresses
     // built from them stay in scalar registers.
     s = wave_uniform(s);
@@ -370,7 +372,9 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     tin = wave_uniform(tin);
     ntile = wave_uniform(ntile);
     whole = wave_uniform(int(whole)) != 0;
-    rec_base = wave_uniform64(rec_base);
+    slots.fixed = wave_uniform64(slots.fixed);
+    slots.overflow = wave_uniform64(slots.overflow);
+    k0 = wave_uniform(k0);
     const int t_begin = tin * kTile;
     const int t_end = min(L, (tin + ntile) * kTile);
     const int nblk = (L + B - 1) / B;
@@ -429,8 +433,8 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
           if (col == 0) rec_lds[base + G * D + 2 * G] = __uint_as_float(a.epoch);
         }
       }
-      if (lane == 0) rec_dst[staged] = rec_base + p;
-      if (++staged == slots) drain();
+      if (lane == 0) rec_dst[staged] = record_slot(slots, k0 + p);
+      if (++staged == stage_slots) drain();
     };
     // The run's end: the output itself for a whole pair, else the last
     // partition's record.
@@ -577,7 +581,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       for (int i = lane; i < G * D; i += kThreads) o[i] = 0;
       return;
     }
-    run(s, kvh, L, 0, (L + kTile - 1) / kTile, true, 0);
+    run(s, kvh, L, 0, (L + kTile - 1) / kTile, true, PairSlots{0, 0}, 0);
   }
 }
 

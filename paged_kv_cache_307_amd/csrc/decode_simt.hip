@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64) void decode_simt_kernel(DecodeArgs a, int B) {
   __shared__ float p_s[kGMax][64];
   __shared__ int64_t vbase_s[64];
 
-  auto piece = [&](int s, int kvh, int L, int tin, int ntile, bool whole, int64_t rec_index) {
+  auto piece = [&](int s, int kvh, int L, int tin, int ntile, bool whole, int64_t rec_slot) {
     // Every argument is the same in all lanes; say so, so that addresses
     // built from them stay in scalar registers.
     s = wave_uniform(s);
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64) void decode_simt_kernel(DecodeArgs a, int B) {
     tin = wave_uniform(tin);
     ntile = wave_uniform(ntile);
     whole = wave_uniform(int(whole)) != 0;
-    rec_index = wave_uniform64(rec_index);
+    rec_slot = wave_uniform64(rec_slot);
     const int t_begin = 16 * tin;
     const int t_end = min(L, 16 * (tin + ntile));
     const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(64) void decode_simt_kernel(DecodeArgs a, int B) {
       __syncthreads();
     }
 
-    float* rec = whole ? nullptr : a.ws + rec_index * record_floats(G, D);
+    float* rec = whole ? nullptr : a.ws + rec_slot * record_floats(G, D);
 #pragma unroll
     for (int h = 0; h < kGMax; ++h) {
       if (h >= G) continue;

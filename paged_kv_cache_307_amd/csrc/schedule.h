@@ -10,13 +10,16 @@
 //
 // A worker cuts its slice into pieces at pair boundaries and at partition
 // boundaries (every partition_size tokens of a pair).  Each piece yields one
-// log-sum-exp record, stored at index  gp + b,  gp being the global index of
+// log-sum-exp record with line index  gp + b,  gp being the global index of
 // the partition the piece lies in (partitions numbered along the line, pair
 // (s, g) starting at Hkv * prefP[s] + g * nparts_s, prefP the exclusive
 // prefix of nparts_s = ceil(L_s / partition_size)).  Along the line every
 // cut raises gp or b (or both), so indices are distinct and below
-// total_partitions + W.  A piece that is a whole pair writes the final
-// output instead of a record.  The merge walks the same cuts per pair.
+// total_partitions + W, and a pair's records have consecutive indices
+// k = 0, 1, ... from its first.  The first few of them are stored at slots
+// indexed by the pair instead (PairSlots below).  A piece that is a whole
+// pair writes the final output instead of a record.  The merge walks the
+// same cuts per pair.
 // (A worker may stream one pair's pieces back to back as a single run,
 // writing each partition's record as it passes the partition's end.)
 #pragma once
@@ -28,22 +31,50 @@ namespace pa {
 // Largest worker grid the workspace is sized for.
 constexpr int kMaxWorkers = 4096;
 
+// A pair's records are numbered k = 0, 1, ... in line order (k = partition
+// + worker - the worker of the pair's first tile).  The first kPairSlots of
+// them have slots of their own, indexed by the pair, so the merge can load
+// them without first finding where the pair's records start; the others sit
+// in an overflow region at their line index (global partition + worker).
+constexpr int kPairSlots = 4;
+
 // Workspace layout (bytes): int32 prefT[S], int32 prefP[S], int64 N and
-// uint32 epoch (at an 8-aligned offset), padding to 256, then the records.
+// uint32 epoch (at an 8-aligned offset), padding to 256, then the records:
+// S * Hkv * kPairSlots pair slots, then the overflow region.
 __host__ __device__ inline int64_t meta_bytes(int num_seqs) {
   const int64_t n_off = (int64_t(num_seqs) * 8 + 7) / 8 * 8;
   return (n_off + 16 + 255) / 256 * 256;
 }
 __host__ __device__ inline int64_t max_records(int num_seqs, int num_kv_heads, int64_t max_parts) {
-  return int64_t(num_seqs) * num_kv_heads * max_parts + kMaxWorkers;
+  return int64_t(num_seqs) * num_kv_heads * (kPairSlots + max_parts) + kMaxWorkers;
+}
+
+// Where the records of one pair live.
+struct PairSlots {
+  int64_t fixed;     // slot of record 0 among the pair slots: pair index * kPairSlots
+  int64_t overflow;  // overflow slot of record 0: S * Hkv * kPairSlots + line index of record 0
+};
+__device__ __forceinline__ int64_t record_slot(const PairSlots& p, int k) {
+  return k < kPairSlots ? p.fixed + k : p.overflow + k;
+}
+
+// floor(p / q) for 0 <= p < 2^53 and 1 <= q < 2^53, through one double
+// division instead of a 64-bit integer division (which the GPU runs as a
+// long software sequence).  Exact: p and q are exact in double and the
+// quotient is rounded once, with an error below (p / q) * 2^-53 < 1 / q;
+// an integer quotient is exact, and any other lies at least 1 / q from the
+// next integer, so the rounding never crosses one.  The line length N is
+// kept below 2^40 by the host, so N * W < 2^52 here.
+__device__ __forceinline__ int64_t floor_div_small(int64_t p, int64_t q) {
+  return int64_t(floor(double(p) / double(q)));
 }
 
 __device__ __forceinline__ int64_t slice_start(int64_t n, int workers, int b) {
-  return n * b / workers;
+  return floor_div_small(n * b, workers);
 }
 // The worker whose slice holds line position x (0 <= x < n).
 __device__ __forceinline__ int owner_of(int64_t n, int workers, int64_t x) {
-  return int(((x + 1) * workers - 1) / n);
+  return int(floor_div_small((x + 1) * workers - 1, n));
 }
 
 struct PairShape {
@@ -139,13 +170,14 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
   return r;
 }
 
-// Calls run(s, g, L, first_tile, num_tiles, whole, rec_base) for every run
+// Calls run(s, g, L, first_tile, num_tiles, whole, slots, k0) for every run
 // of consecutive tiles of one pair in worker b's slice, in line order.  A
 // run ends only at a pair boundary or at the slice's end; it may span
 // several partitions, and the tiles of the pair's partition p (p = tile *
-// 16 / partition_size) belong to the record at index rec_base + p.  whole:
-// the run is the entire pair and the pair has one partition, so the output
-// is written directly and no record is made.
+// 16 / partition_size) make the pair's record k0 + p, stored at
+// record_slot(slots, k0 + p).  whole: the run is the entire pair and the
+// pair has one partition, so the output is written directly and no record
+// is made.
 template <typename RunFn>
 __device__ __forceinline__ void walk_slice_runs(const DecodeArgs& a, int block_size, int lane,
                                                 int b, RunFn&& run) {
@@ -177,12 +209,17 @@ __device__ __forceinline__ void walk_slice_runs(const DecodeArgs& a, int block_s
     const int64_t end = min(sbase + int64_t(g + 1) * ps.tiles, sl.x1);
     const int ntile = int(end - cur);
     const bool whole = tin == 0 && ntile == ps.tiles && ps.parts == 1;
-    run(s, g, len, tin, ntile, whole, gpb + int64_t(g) * ps.parts + b);
+    const int64_t pair_base = sbase + int64_t(g) * ps.tiles;
+    const int b_first = owner_of(sl.n, a.workers, pair_base);
+    PairSlots slots;
+    slots.fixed = (int64_t(s) * Hkv + g) * kPairSlots;
+    slots.overflow = int64_t(a.num_seqs) * Hkv * kPairSlots + gpb + int64_t(g) * ps.parts + b_first;
+    run(s, g, len, tin, ntile, whole, slots, b - b_first);
     cur = end;
   }
 }
 
-// Calls piece(s, g, L, first_tile, num_tiles, whole, record_index) for
+// Calls piece(s, g, L, first_tile, num_tiles, whole, record_slot) for
 // every piece of worker b's slice, in line order: the runs above, cut
 // further at partition boundaries.
 template <typename PieceFn>
@@ -190,47 +227,60 @@ __device__ __forceinline__ void walk_slice(const DecodeArgs& a, int block_size, 
                                            PieceFn&& piece) {
   const int tpp = a.partition_size / 16;  // tiles per partition
   walk_slice_runs(a, block_size, lane, b,
-                  [&](int s, int g, int len, int tin, int ntile, bool whole, int64_t rec_base) {
+                  [&](int s, int g, int len, int tin, int ntile, bool whole,
+                      const PairSlots& slots, int k0) {
                     if (whole) {
-                      piece(s, g, len, tin, ntile, true, rec_base);
+                      piece(s, g, len, tin, ntile, true, int64_t(0));
                       return;
                     }
                     const int end = tin + ntile;
                     for (int t = tin; t < end;) {
                       const int part = t / tpp;
                       const int e = min(end, (part + 1) * tpp);
-                      piece(s, g, len, t, e - t, false, rec_base + part);
+                      piece(s, g, len, t, e - t, false, record_slot(slots, k0 + part));
                       t = e;
                     }
                   });
 }
 
-// Record indices of pair (s, g): every piece of the pair has an index in
-// [first, last]; indices in that range that belong to no piece (a worker cut
-// falling on a partition cut skips one) hold records of older launches,
-// whose epoch differs.  Needs the meta block written by worker 0.  Returns
-// false when the pair has no tiles.
+// The records of pair (s, g): records 0 .. count - 1, at
+// record_slot(slots, k).  Some k in that range belong to no piece (a worker
+// cut falling on a partition cut skips one); their slots hold records of
+// older launches, whose epoch differs.  Needs the meta block written by
+// worker 0.  Returns false when the pair has no tiles.
 struct PairRecords {
-  int64_t first, last;
+  PairSlots slots;
+  int count;
   bool whole;      // one piece: its worker wrote the output directly
   uint32_t epoch;  // stamp of the launch that wrote the meta block
 };
 
+// Slots of pair (s, g) that need no meta block (pair slots only).
+__device__ __forceinline__ int64_t pair_fixed_slot(const DecodeArgs& a, int s, int g) {
+  return (int64_t(s) * a.num_kv_heads + g) * kPairSlots;
+}
+
 __device__ __forceinline__ bool pair_records(const DecodeArgs& a, int block_size, int s, int g,
                                              PairRecords* pr) {
-  const PairShape ps = pair_shape(a, s, block_size);
-  if (ps.tiles == 0) return false;
+  // the meta loads go out with the length's, not after it
   const int32_t* meta = reinterpret_cast<const int32_t*>(a.ws_meta);
   const int64_t n = *meta_n(a);
+  const int32_t pref_t = meta[s];
+  const int32_t pref_p = meta[a.num_seqs + s];
+  const uint32_t epoch = *reinterpret_cast<const uint32_t*>(meta_n(a) + 1);
+  asm volatile("" ::: "memory");
+  const PairShape ps = pair_shape(a, s, block_size);
+  if (ps.tiles == 0) return false;
   const int Hkv = a.num_kv_heads;
-  const int64_t base = int64_t(meta[s]) * Hkv + int64_t(g) * ps.tiles;
-  const int64_t gp0 = int64_t(meta[a.num_seqs + s]) * Hkv + int64_t(g) * ps.parts;
+  const int64_t base = int64_t(pref_t) * Hkv + int64_t(g) * ps.tiles;
+  const int64_t gp0 = int64_t(pref_p) * Hkv + int64_t(g) * ps.parts;
   const int b_first = owner_of(n, a.workers, base);
   const int b_last = owner_of(n, a.workers, base + ps.tiles - 1);
-  pr->first = gp0 + b_first;
-  pr->last = gp0 + ps.parts - 1 + b_last;
+  pr->slots.fixed = pair_fixed_slot(a, s, g);
+  pr->slots.overflow = int64_t(a.num_seqs) * Hkv * kPairSlots + gp0 + b_first;
+  pr->count = ps.parts + b_last - b_first;
   pr->whole = b_first == b_last && ps.parts == 1;
-  pr->epoch = *reinterpret_cast<const uint32_t*>(meta_n(a) + 1);
+  pr->epoch = epoch;
   return true;
 }
 

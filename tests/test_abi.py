@@ -86,6 +86,9 @@ def decode_call(lib, fn="pa_decode", **kw):
     (dict(S=0, out=None, q=None), OK),
     # split schedule: sequences x 16-token tiles must fit in 31 bits
     (dict(S=1 << 20, MB=4096, maxlen=1 << 16, P=512, ws=FAKE, wsb=1 << 40), UNSUPPORTED),
+    # ... and the whole line (tiles x KV heads) below 2^40
+    (dict(S=1 << 19, Hq=1024, Hkv=1024, MB=2048, maxlen=1 << 15, P=512, ws=FAKE, wsb=1 << 62),
+     UNSUPPORTED),
 ])
 def test_decode_rejects_before_launch(lib, fn, kw, expect):
     assert decode_call(lib, fn, **kw) == expect
@@ -125,14 +128,15 @@ def test_write_and_copy_reject_before_launch(lib):
 
 def test_workspace_size_formula(lib):
     # meta block (int32 prefT[S], prefP[S], int64 N, uint32 epoch, padded to
-    # 256 bytes), then S*Hkv*max(1, ceil(L/P)) + 4096 records of o[G][D],
-    # m[G], l[G] and a stamp, padded to a multiple of 4 floats
+    # 256 bytes), then S*Hkv*(4 + max(1, ceil(L/P))) + 4096 records (four
+    # pair slots per pair, then the overflow region) of o[G][D], m[G], l[G]
+    # and a stamp, padded to a multiple of 4 floats
     def expect(S, Hq, Hkv, D, L, P):
         G = Hq // Hkv
         parts = max(1, -(-L // P))
         rec = G * D + (2 * G + 1 + 3) // 4 * 4
         meta = ((S * 8 + 7) // 8 * 8 + 16 + 255) // 256 * 256
-        return meta + (S * Hkv * parts + 4096) * rec * 4
+        return meta + (S * Hkv * (4 + parts) + 4096) * rec * 4
     for args in [(64, 32, 8, 128, 4096, 512), (8, 32, 8, 128, 131072, 512), (3, 5, 5, 64, 100, 16),
                  (256, 64, 8, 128, 8192, 512), (4, 32, 8, 128, 512, 512), (2, 4, 2, 64, 0, 16)]:
         assert pa.decode_workspace_bytes(*args) == expect(*args), args

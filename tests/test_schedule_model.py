@@ -17,13 +17,18 @@ kernels rely on, over random length mixes and worker counts:
 * every record of a pair lies in the range the merge scans for it, and no
   record of another pair does (indices grow along the line);
 * a pair is "whole" (one piece, output written directly) exactly when the
-  merge range has a single index and the pair has one partition.
+  merge range has a single index and the pair has one partition;
+* with the first PAIR_SLOTS records of each pair (numbered k from the start
+  of its merge range) moved to slots indexed by the pair, slots stay
+  distinct and within the workspace, and the merge's slots for k < count
+  hold exactly the pair's records (or nothing of this launch).
 """
 
 import numpy as np
 import pytest
 
 TILE = 16
+PAIR_SLOTS = 4
 
 
 def slice_start(n, workers, b):
@@ -146,6 +151,36 @@ def test_schedule_invariants(case):
             for r in range(first, last + 1):  # indices in range: this pair's, or unused
                 assert owner.get(r, (s, g)) == (s, g)
 
+    # pair slots: record k of a pair (k = line index - first index of its
+    # merge range) goes to pair * PAIR_SLOTS + k when k < PAIR_SLOTS, else to
+    # the overflow region at S * Hkv * PAIR_SLOTS + its line index
+    S = len(lengths)
+    slot_of = {}
+    for r, s_, g_ in recs:
+        first, last, _ = merge_range(lengths, hkv, partition, workers, n, s_, g_)
+        k = r - first
+        assert 0 <= k <= last - first
+        slot_of[r] = (s_ * hkv + g_) * PAIR_SLOTS + k if k < PAIR_SLOTS else S * hkv * PAIR_SLOTS + r
+    slots = list(slot_of.values())
+    assert len(slots) == len(set(slots))
+    assert all(0 <= x < S * hkv * (PAIR_SLOTS + max(parts + [1])) + workers for x in slots)
+    by_slot = {x: r for r, x in slot_of.items()}
+    for s in range(len(lengths)):
+        if tiles[s] == 0:
+            continue
+        for g in range(hkv):
+            first, last, whole = merge_range(lengths, hkv, partition, workers, n, s, g)
+            if whole:
+                continue
+            seen_recs = set()
+            for k in range(last - first + 1):
+                x = (s * hkv + g) * PAIR_SLOTS + k if k < PAIR_SLOTS else S * hkv * PAIR_SLOTS + first + k
+                r = by_slot.get(x)
+                if r is not None:
+                    assert owner[r] == (s, g)
+                    seen_recs.add(r)
+            assert seen_recs == {r for r, ss, gg in recs if (ss, gg) == (s, g)}
+
 
 def test_workspace_record_bound_is_tight_enough():
     """The host sizes the records as S * Hkv * ceil(L_max / P) + 4096; with
@@ -154,3 +189,26 @@ def test_workspace_record_bound_is_tight_enough():
     ps, n = pieces(lengths, 8, 512, 4096)
     cap = 8 * 8 * (4096 // 512) + 4096
     assert max(p[6] for p in ps if not p[5]) < cap
+
+
+def test_double_floor_division_is_exact_below_2_53():
+    """The schedule divides line positions with one IEEE double division and
+    a floor (p < 2^53, q < 2^53); Python floats are IEEE doubles, so this
+    checks the claim that the result equals integer floor division."""
+    import math
+    rng = np.random.default_rng(307_301)
+    cases = []
+    for _ in range(20000):
+        q = int(rng.integers(1, 1 << int(rng.integers(1, 53))))
+        p = int(rng.integers(0, 1 << 53))
+        cases.append((p, q))
+        k = p // q
+        for d in (-1, 0, 1):       # next to multiples of q
+            if 0 <= k * q + d < (1 << 53):
+                cases.append((k * q + d, q))
+    # the largest operands the decode forms: N < 2^40 tiles, W <= 4096
+    for n in ((1 << 40) - 1, (1 << 40) - 3, 3 * (1 << 38) + 7):
+        for w in (4096, 4095, 768, 1):
+            cases += [(n * w, w), (n * w - 1, n), ((n - 1 + 1) * w - 1, n)]
+    for p, q in cases:
+        assert math.floor(float(p) / float(q)) == p // q, (p, q)
