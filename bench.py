@@ -57,8 +57,8 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False): {
-        "bytes": 552518736, "fetch_bytes": 547658996, "write_bytes": 4859740,
-        "sources_sha256": "a1a7012a270d9cb014576ef13880f3266249c52a6ea3dae2c56899e08c88d48f"},
+        "bytes": 552453698, "fetch_bytes": 547587554, "write_bytes": 4866144,
+        "sources_sha256": "bda67d03559c3461e42e4ef6c1c9cfc9df3a0f84eea2016186f79b30b1c52f86"},
 }
 
 
