@@ -9,9 +9,12 @@
 // FlashAttention technique the pages say composes with paged storage (P2,
 // comparison with FlashAttention).
 //
-// Work decomposition.  One workgroup of 4 waves per (sequence, KV head,
-// partition).  The partition's tokens are cut into 16-token tiles; wave w
-// takes tiles w, w+4, ...  A tile is the unit of both matrix-core products:
+// Work decomposition.  Each (sequence, KV head) pair's tokens are cut into
+// 16-token tiles.  Split launches run a fixed set of single-wave workers
+// that share the tiles of all pairs equally (schedule.h); each streams its
+// share pair by pair and leaves log-sum-exp records for the merge.  Single
+// pass runs one wave per pair.  A tile is the unit of both matrix-core
+// products:
 //
 //   S^T[16 tok x 16 col] = K_tile[16 tok x D] . Q^T[D x 16 col]  (16x16x32 bf16, D/32 steps)
 //   O^T[D x 16 col]     += V^T_tile[D x 16 tok] . P^T[16 tok x 16 col] (16x16x16 bf16, D/16)
@@ -124,8 +127,9 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // ~6.4 TB/s.  When blocks are shared between sequences the default policy
 // keeps them in the caches for their other readers.  With B = 32 a 16-token
 // V tile covers half of each 128-byte line and the next tile reads the other
-// half from the L2; streaming V there costs more than it saves, and
-// streaming K alone measured slower than the default policy for both.
+// half from the L2: streaming V there costs more than it saves, streaming K
+// alone measured slower than the default policy for both, and even 8 KiB
+// block reads (both halves at once) gain nothing from the nt bit.
 constexpr int kStreamOnce = 2;
 
 template <int B, bool kStream>
@@ -272,27 +276,47 @@ __device__ __forceinline__ void put_new_row(Tile<D>& r, const uint32_t* lds, int
   }
 }
 
-// Store the new row at position p of the pair, block pb (a valid id).
+// Appending decode: write the tile holding the step's token back to the
+// cache once the token's row is in its registers (before the tile is masked
+// for consumption): the token's K row from the lanes of row rt, and the
+// tile's V rows whole, every lane's 8 bytes, the other tokens' values being
+// the ones just read.  The token's V column thus leaves as full 32-byte row
+// segments (2 KiB of 4 KiB tile rows at D = 128) instead of D two-byte
+// stores at a 32-byte stride, each of which HBM has to merge into its
+// sector.  Only lanes whose rows lie in the token's block pb store (a B = 8
+// tile spans two blocks).  Only this wave touches that block in this launch.
 template <int D, int B>
-__device__ __forceinline__ void store_new_row(const DecodeArgs& a, const NewRow<D>& nr, int pb,
-                                              int kvh, int p, int lane) {
-  constexpr int E = NewRow<D>::kElems;
-  if (lane >= NewRow<D>::kLanes) return;
-  const int64_t tile = int64_t(pb) * a.num_kv_heads + kvh;
+__device__ __forceinline__ void store_tile_back(const Tile<D>& r, const DecodeArgs& a, int pb,
+                                                int kvh, int t0, int rt, int lane,
+                                                uint32_t k_off, uint32_t v_off) {
+  constexpr int kTileBytes = B * D * 2;
   // the pools are writable when a row is appended (the API takes them non-const)
-  uint16_t* kd = static_cast<uint16_t*>(const_cast<void*>(a.k_cache)) + (tile * B + p % B) * D +
-                 lane * E;
-  uint16_t* vd = static_cast<uint16_t*>(const_cast<void*>(a.v_cache)) +
-                 (tile * D + lane * E) * B + p % B;
-  if constexpr (E == 2) {
-    *reinterpret_cast<uint32_t*>(kd) = nr.k[0];
-  } else {
-    *reinterpret_cast<uint2*>(kd) = make_uint2(nr.k[0], nr.k[1]);
+  char* kc = static_cast<char*>(const_cast<void*>(a.k_cache));
+  char* vc = static_cast<char*>(const_cast<void*>(a.v_cache));
+  const int64_t tile = (int64_t(pb) * a.num_kv_heads + kvh) * kTileBytes;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  bool v_here = true;
+  int64_t k_shift = 0, v_shift = 0;
+  if constexpr (B >= kTile) {
+    const int in_block = t0 % B;  // 0, or 16 when B == 32
+    k_shift = in_block * D * 2;
+    v_shift = in_block * 2;
+  } else {  // the tile's second block holds tokens B .. 15
+    const bool second = rt >= B;
+    k_shift = second ? -int64_t(B) * D * 2 : 0;
+    v_shift = second ? -int64_t(B) * 2 : 0;
+    v_here = (grp >= 2) == second;
   }
+  if (col == rt) {
+    char* kb = kc + tile + k_shift + k_off;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t dw = nr.v[e / 2];
-    vd[e * B] = uint16_t((e % 2) ? dw >> 16 : dw & 0xFFFFu);
+    for (int j = 0; j < D / 32; ++j) *reinterpret_cast<uint4*>(kb + 64 * j) = r.k[j];
+  }
+  if (v_here) {
+    char* vb = vc + tile + v_shift + v_off;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) *reinterpret_cast<uint2*>(vb + 32 * B * c) = r.v[c];
   }
 }
 
@@ -359,11 +383,11 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   const uint32_t v_off = uint32_t(col) * B * 2 + uint32_t(grp) * 8;
 
   // One run: tiles [tin, tin + ntile) of pair (s, kvh).  The tiles of the
-  // pair's partition p make its record k0 + p (stored at record_slot(slots,
-  // k0 + p)), or, when the run is the whole pair (one partition), go
-  // straight to the output.
+  // pair's partition p make its record k_first + p (stored at
+  // record_slot(slots, k_first + p)), or, when the run is the whole pair (one
+  // partition), go straight to the output.
   auto run = [&](int s, int kvh, int L, int tin, int ntile, bool whole, PairSlots slots,
-                 int k0) {
+                 int k_first) {
     // Every argument is the same in all lanes; say so, so that addresses
     // built from them stay in scalar registers.
     s = wave_uniform(s);
@@ -374,14 +398,15 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     whole = wave_uniform(int(whole)) != 0;
     slots.fixed = wave_uniform64(slots.fixed);
     slots.overflow = wave_uniform64(slots.overflow);
-    k0 = wave_uniform(k0);
+    k_first = wave_uniform(k_first);
     const int t_begin = tin * kTile;
     const int t_end = min(L, (tin + ntile) * kTile);
     const int nblk = (L + B - 1) / B;
     const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
 
-    // Appending decode: the run holding the pair's last tile writes the
-    // step's row (token L - 1) to its slot and uses it in that tile.
+    // Appending decode: the run holding the pair's last tile uses the step's
+    // row (token L - 1) in that tile and writes the tile back with the row
+    // in its slot.
     const bool append = a.new_k != nullptr && tin + ntile == (L + kTile - 1) / kTile;
     NewRow<D> nr{};
     int pb_new = 0;
@@ -433,7 +458,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
           if (col == 0) rec_lds[base + G * D + 2 * G] = __uint_as_float(a.epoch);
         }
       }
-      if (lane == 0) rec_dst[staged] = record_slot(slots, k0 + p);
+      if (lane == 0) rec_dst[staged] = record_slot(slots, k_first + p);
       if (++staged == stage_slots) drain();
     };
     // The run's end: the output itself for a whole pair, else the last
@@ -517,11 +542,9 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       Tile<D> ring[kRing];
       int win = load_window(row, t_begin / B, nblk, lane);
       if (append) {
-        // the row goes to LDS for the last tile, and to its slot in the cache
-        // (only this wave reads that slot in this launch)
+        // the row goes to LDS for the last tile, which also writes it to its
+        // slot in the cache (only this wave reads that slot in this launch)
         stage_new_row<D>(nr, new_row_lds, lane);
-        if (unsigned(pb_new) < unsigned(a.num_blocks))
-          store_new_row<D, B>(a, nr, pb_new, kvh, L - 1, lane);
       }
       for (int k0 = 0; k0 < ntile; k0 += kWin) {
         const int k1 = min(ntile, k0 + kWin);
@@ -545,8 +568,13 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                                      k_off, v_off);
             id = window_ids<B>(win, wb, t0_of(min(k + d + kRing, last)), nblk);
             if (k + d < k1) {
-              if (append && k + d == ntile - 1)
-                put_new_row<D>(ring[d], new_row_lds, t_end - 1 - t0_of(k + d), col, grp);
+              if (append && k + d == ntile - 1) {
+                const int rt = t_end - 1 - t0_of(k + d);
+                put_new_row<D>(ring[d], new_row_lds, rt, col, grp);
+                if (unsigned(pb_new) < unsigned(a.num_blocks))
+                  store_tile_back<D, B>(ring[d], a, pb_new, kvh, t0_of(k + d), rt, lane, k_off,
+                                        v_off);
+              }
               consume(ring[d], k + d);
               if (kParts && --part_left == 0 && k + d + 1 < ntile) {
                 stage(part);
