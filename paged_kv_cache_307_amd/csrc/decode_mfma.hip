@@ -347,6 +347,16 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   constexpr int kMaxStaged = kSplit ? 16 : 1;
   __shared__ __align__(16) float rec_lds[kRecLdsFloats];
   __shared__ int64_t rec_dst[kMaxStaged];
+  // Appending split workers keep their write-back tiles here too (the V rows
+  // of every lane and the token's K row) and store them after their last
+  // run, for the same reason: stored in mid-stream they held up the next
+  // run's first loads.  Two tiles, 4.25 KiB each at D = 128; a worker with
+  // more appending runs stores the others at once.
+  constexpr int kTbSlots = kSplit ? 2 : 0;
+  constexpr int kTbDwords = D * 8 + D / 2;  // V: D/16 x 64 lanes x 2; K: D/32 x 4 lanes x 4
+  __shared__ __align__(16) uint32_t tb_lds[kTbSlots > 0 ? kTbSlots * kTbDwords : 1];
+  __shared__ int tb_info[kTbSlots > 0 ? kTbSlots * 4 : 1];  // block, kvh, tile start, row
+  int tb_used = 0;
   const int rec_f = int(record_floats(G, D));
   const int stage_slots = min(kMaxStaged, kRecLdsFloats / rec_f);
   int staged = 0;  // records waiting in LDS
@@ -381,6 +391,52 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   // Per-lane byte offsets inside a tile.
   const uint32_t k_off = uint32_t(col) * D * 2 + uint32_t(grp) * 16;
   const uint32_t v_off = uint32_t(col) * B * 2 + uint32_t(grp) * 8;
+
+  // Keeps an appending tile's write-back for later (see tb_lds), or stores
+  // it now when both slots are taken.
+  auto write_back = [&](const Tile<D>& r, int pb, int kvh, int t0, int rt) {
+    if (tb_used == kTbSlots) {
+      store_tile_back<D, B>(r, a, pb, kvh, t0, rt, lane, k_off, v_off);
+      return;
+    }
+    uint32_t* slot = tb_lds + tb_used * kTbDwords;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c)
+      *reinterpret_cast<uint2*>(slot + (c * kThreads + lane) * 2) = r.v[c];
+    if (col == rt) {
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        *reinterpret_cast<uint4*>(slot + D * 8 + (j * 4 + grp) * 4) = r.k[j];
+    }
+    if (lane == 0) {
+      tb_info[tb_used * 4 + 0] = pb;
+      tb_info[tb_used * 4 + 1] = kvh;
+      tb_info[tb_used * 4 + 2] = t0;
+      tb_info[tb_used * 4 + 3] = rt;
+    }
+    ++tb_used;
+  };
+  // Stores the kept write-backs.
+  auto flush_write_backs = [&]() {
+    __syncthreads();  // one wave: orders the LDS writes before the reads
+    for (int i = 0; i < tb_used; ++i) {
+      const uint32_t* slot = tb_lds + i * kTbDwords;
+      const int pb = wave_uniform(tb_info[i * 4 + 0]);
+      const int kvh = wave_uniform(tb_info[i * 4 + 1]);
+      const int t0 = wave_uniform(tb_info[i * 4 + 2]);
+      const int rt = wave_uniform(tb_info[i * 4 + 3]);
+      Tile<D> r;
+#pragma unroll
+      for (int c = 0; c < DCH; ++c)
+        r.v[c] = *reinterpret_cast<const uint2*>(slot + (c * kThreads + lane) * 2);
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        r.k[j] = *reinterpret_cast<const uint4*>(slot + D * 8 + (j * 4 + grp) * 4);
+      r.bad = false;
+      store_tile_back<D, B>(r, a, pb, kvh, t0, rt, lane, k_off, v_off);
+    }
+    tb_used = 0;
+  };
 
   // One run: tiles [tin, tin + ntile) of pair (s, kvh).  The tiles of the
   // pair's partition p make its record k_first + p (stored at
@@ -572,8 +628,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                 const int rt = t_end - 1 - t0_of(k + d);
                 put_new_row<D>(ring[d], new_row_lds, rt, col, grp);
                 if (unsigned(pb_new) < unsigned(a.num_blocks))
-                  store_tile_back<D, B>(ring[d], a, pb_new, kvh, t0_of(k + d), rt, lane, k_off,
-                                        v_off);
+                  write_back(ring[d], pb_new, kvh, t0_of(k + d), rt);
               }
               consume(ring[d], k + d);
               if (kParts && --part_left == 0 && k + d + 1 < ntile) {
@@ -598,6 +653,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
   if constexpr (kSplit) {
     walk_slice_runs(a, B, lane, blockIdx.x, run);
     if (staged > 0) drain();
+    if (tb_used > 0) flush_write_backs();
   } else {
     // one worker per (sequence, KV head); consecutive workers are the KV
     // heads of one sequence (workgroup i runs on XCD i % 8)
