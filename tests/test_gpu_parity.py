@@ -264,6 +264,20 @@ def test_partition_records_staged_and_drained(shape):
                 append=True, two_phase=True)
 
 
+@pytest.mark.parametrize("shape", [(32, 8, 128, 16), (16, 4, 64, 8), (16, 2, 256, 32)])
+def test_append_many_short_sequences(shape):
+    """Hundreds of 1..40-token sequences: each split worker holds the last
+    tile of several pairs, so it keeps two write-back tiles in LDS and
+    stores the rest at once; the pools must match the oracle bit for bit."""
+    Hq, Hkv, D, B = shape
+    rng = np.random.default_rng(307_047 + D)
+    lengths = [int(x) for x in rng.integers(1, 41, size=640 if D < 256 else 320)]
+    w = W.custom(lengths, Hq, Hkv, D, B, "bf16", seed=307_048 + D + B)
+    ref = oracle.run_step(w)
+    for P in (0, 16 if B <= 16 else 32, 64):
+        _check_step(w, P, ref=ref, append=True, two_phase=P > 0)
+
+
 def test_single_token_is_exact_copy():
     """L = 1: the output is the token's V row, bit for bit after rounding."""
     w = W.custom([1, 1, 1], 8, 4, 128, 16, "bf16", seed=307_051)
