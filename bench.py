@@ -57,8 +57,8 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False): {
-        "bytes": 552453698, "fetch_bytes": 547587554, "write_bytes": 4866144,
-        "sources_sha256": "bda67d03559c3461e42e4ef6c1c9cfc9df3a0f84eea2016186f79b30b1c52f86"},
+        "bytes": 553895046, "fetch_bytes": 549028902, "write_bytes": 4866144,
+        "sources_sha256": "609c5e8a8dae5a6c33642f6db3ab593f8fd19b04c216e59ef11142b2b5ae5dcf"},
 }
 
 
