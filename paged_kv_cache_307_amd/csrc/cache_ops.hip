@@ -9,9 +9,10 @@
 // The appending form of the write takes the slot of each sequence's last
 // position from its block table (the decode step's own token).
 //
-// All of them are HBM-bound byte movers; each 64-lane wave moves whole 16-byte
-// vectors where the layout is contiguous (K rows, whole blocks) and single
-// elements where it is strided (V's token-innermost rows).
+// All of them are HBM-bound byte movers.  They move whole 16-byte vectors
+// where the layout is contiguous (K rows, whole blocks, and V rows of blocks
+// the write fills, transposed through LDS) and single elements where it is
+// strided (V's token-innermost rows of a lone token).
 
 #include "device_common.h"
 
@@ -68,18 +69,135 @@ __device__ __forceinline__ void store_row(Elem* __restrict__ k_cache, Elem* __re
   }
 }
 
-// One workgroup per token row i, stored at slot_mapping[i].
+// Rows per workgroup of the write.
+constexpr int kWriteChunk = 256;
+// Largest (block, KV head) V tile the write transposes through LDS.
+constexpr int kTileLdsBytes = 32768;
+
+// One wave stores one token row at (block, off), all KV heads: K rows as
+// 16-byte vectors, V one element per (head, dim) at stride block_size.
+template <typename Elem>
+__device__ __forceinline__ void store_row_wave(Elem* __restrict__ k_cache,
+                                               Elem* __restrict__ v_cache,
+                                               const Elem* __restrict__ key_row,
+                                               const Elem* __restrict__ value_row, int64_t block,
+                                               int off, int num_kv_heads, int head_dim,
+                                               int block_size, int lane) {
+  const int row = num_kv_heads * head_dim;
+  const int64_t block_elems = int64_t(row) * block_size;
+  constexpr int kVec = 16 / sizeof(Elem);
+  const int dim_vecs = head_dim / kVec;
+  const uint4* src_k = reinterpret_cast<const uint4*>(key_row);
+  for (int v = lane; v < row / kVec; v += 64) {
+    const int h = v / dim_vecs;
+    Elem* dst = k_cache + block * block_elems + (int64_t(h) * block_size + off) * head_dim;
+    reinterpret_cast<uint4*>(dst)[v % dim_vecs] = src_k[v];
+  }
+  Elem* vblk = v_cache + block * block_elems + off;
+  for (int e = lane; e < row; e += 64) vblk[int64_t(e) * block_size] = value_row[e];  // [h][d][off]
+}
+
+// The write of rows [c0, c0 + n) of a slot mapping, n <= kWriteChunk.
+//
+// Rows usually come sequence by sequence with ascending positions, so most
+// blocks receive all B of their slots, in order, from B consecutive rows.
+// Such a block is written as whole (block, KV head) tiles: K rows as 16-byte
+// vectors, and V transposed through LDS so that each dim's row of B tokens
+// leaves as full 16-byte vectors.  Storing a V column one element at a time
+// (token-innermost layout) writes 2 of every 2 * B bytes of each row
+// segment, a partial write of a memory sector per element.  Rows of blocks
+// this chunk does not fill (and every row when the tile path does not
+// apply) take the element path, one wave per row.  Slots are distinct (the
+// API's precondition), so a block filled here gets no other row anywhere.
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void write_kv_kernel(
     Elem* __restrict__ k_cache, Elem* __restrict__ v_cache, const Elem* __restrict__ key,
-    const Elem* __restrict__ value, const int64_t* __restrict__ slots, int num_kv_heads,
-    int head_dim, int block_size, int num_blocks) {
-  const int i = blockIdx.x;
-  const int64_t slot = slots[i];
-  if (slot < 0 || slot >= int64_t(num_blocks) * block_size) return;
-  const int64_t row = int64_t(i) * num_kv_heads * head_dim;
-  store_row(k_cache, v_cache, key + row, value + row, slot / block_size, int(slot % block_size),
-            num_kv_heads, head_dim, block_size);
+    const Elem* __restrict__ value, const int64_t* __restrict__ slots, int num_tokens,
+    int num_kv_heads, int head_dim, int block_size, int num_blocks, int tile_path) {
+  __shared__ int64_t s_slot[kWriteChunk];
+  __shared__ int s_start[kWriteChunk];  // row r starts a block this chunk fills
+  __shared__ __align__(16) Elem v_tile[kTileLdsBytes / sizeof(Elem)];
+  const int64_t c0 = int64_t(blockIdx.x) * kWriteChunk;
+  const int n = int(min<int64_t>(kWriteChunk, num_tokens - c0));
+  const int t = threadIdx.x;
+  const int64_t limit = int64_t(num_blocks) * block_size;
+  {
+    int64_t sl = -1;
+    if (t < n) {
+      sl = slots[c0 + t];
+      if (sl < 0 || sl >= limit) sl = -1;  // skipped
+    }
+    s_slot[t] = sl;
+  }
+  __syncthreads();
+  const int B = block_size;
+  {
+    bool start = false;
+    if (tile_path && t < n && t + B <= n && s_slot[t] >= 0 && s_slot[t] % B == 0) {
+      start = true;
+      for (int j = 1; j < B && start; ++j) start = s_slot[t + j] == s_slot[t] + j;
+    }
+    s_start[t] = start;
+  }
+  __syncthreads();
+
+  const int row_elems = num_kv_heads * head_dim;
+  constexpr int kVec = 16 / sizeof(Elem);
+  // whole blocks, one (block, KV head) tile at a time
+  const int dvecs = head_dim / kVec;
+  for (int r = 0; r < n; ++r) {
+    if (!s_start[r]) continue;
+    const int64_t block = s_slot[r] / B;
+    for (int h = 0; h < num_kv_heads; ++h) {
+      const int64_t tile = (block * num_kv_heads + h) * int64_t(B) * head_dim;
+      // K: token j's head-h row is contiguous in the source and the tile
+      for (int v = t; v < B * dvecs; v += kThreads) {
+        const int j = v / dvecs;
+        const int dv = v % dvecs;
+        const Elem* src = key + (c0 + r + j) * row_elems + int64_t(h) * head_dim;
+        reinterpret_cast<uint4*>(k_cache + tile + int64_t(j) * head_dim)[dv] =
+            reinterpret_cast<const uint4*>(src)[dv];
+      }
+      // V: the B rows of head h into LDS as [token][dim], out as [dim][token]
+      for (int v = t; v < B * dvecs; v += kThreads) {
+        const int j = v / dvecs;
+        const int dv = v % dvecs;
+        const Elem* src = value + (c0 + r + j) * row_elems + int64_t(h) * head_dim;
+        reinterpret_cast<uint4*>(v_tile + j * head_dim)[dv] =
+            reinterpret_cast<const uint4*>(src)[dv];
+      }
+      __syncthreads();
+      const int jvecs = B / kVec;
+      for (int v = t; v < head_dim * jvecs; v += kThreads) {
+        const int d = v / jvecs;
+        const int j0 = (v % jvecs) * kVec;
+        Elem e[kVec];
+#pragma unroll
+        for (int u = 0; u < kVec; ++u) e[u] = v_tile[(j0 + u) * head_dim + d];
+        uint4 w;
+        __builtin_memcpy(&w, e, 16);
+        *reinterpret_cast<uint4*>(v_cache + tile + int64_t(d) * B + j0) = w;
+      }
+      __syncthreads();
+    }
+  }
+
+  // the other rows, one wave per row
+  const int wave = t / 64;
+  const int lane = t % 64;
+  for (int i = wave; i < n; i += kThreads / 64) {
+    const int64_t sl = s_slot[i];
+    if (sl < 0) continue;
+    bool in_tile = false;  // covered by a block written above
+    if (tile_path) {
+      const int first = i - int(sl % B);
+      in_tile = first >= 0 && s_start[first];
+    }
+    if (in_tile) continue;
+    const int64_t row = (c0 + i) * row_elems;
+    store_row_wave(k_cache, v_cache, key + row, value + row, sl / B, int(sl % B), num_kv_heads,
+                   head_dim, B, lane);
+  }
 }
 
 // One workgroup per sequence s: its row goes to position L_s - 1 (L_s the
@@ -129,16 +247,25 @@ hipError_t launch_slot_mapping(int64_t* slots, const int32_t* block_tables, cons
 hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const void* value,
                            const int64_t* slots, int num_tokens, int num_kv_heads, int head_dim,
                            int block_size, int num_blocks, int elem_bytes, hipStream_t stream) {
+  // whole-block tiles when a V row of B tokens is whole 16-byte vectors, the
+  // V pool and rows are 16-byte aligned (the ABI asks only element
+  // alignment of them), and one head's V tile fits the LDS buffer
+  const bool v_aligned = (reinterpret_cast<uintptr_t>(v_cache) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(value) % 16 == 0);
+  const int tile_path = v_aligned && (int64_t(block_size) * elem_bytes % 16 == 0) &&
+                        int64_t(block_size) * head_dim * elem_bytes <= kTileLdsBytes &&
+                        block_size <= kWriteChunk;
+  const dim3 grid(unsigned(ceil_div(num_tokens, kWriteChunk)));
   if (elem_bytes == 4) {
-    return launch(write_kv_kernel<uint32_t>, dim3(num_tokens), dim3(kThreads), 0, stream,
+    return launch(write_kv_kernel<uint32_t>, grid, dim3(kThreads), 0, stream,
                   static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
                   static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value), slots,
-                  num_kv_heads, head_dim, block_size, num_blocks);
+                  num_tokens, num_kv_heads, head_dim, block_size, num_blocks, tile_path);
   }
-  return launch(write_kv_kernel<uint16_t>, dim3(num_tokens), dim3(kThreads), 0, stream,
+  return launch(write_kv_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
                 static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
                 static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), slots,
-                num_kv_heads, head_dim, block_size, num_blocks);
+                num_tokens, num_kv_heads, head_dim, block_size, num_blocks, tile_path);
 }
 
 hipError_t launch_append_kv(const DecodeArgs& a, int head_dim, int block_size, int elem_bytes,

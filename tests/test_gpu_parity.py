@@ -6,6 +6,8 @@ small sizes element by element and at the five full workload sizes on every
 or on sampled (sequence, KV head) units.
 """
 
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -315,6 +317,40 @@ def test_copy_blocks_bit_exact_and_skips_bad_ids():
     kb, vb = ref["k_pool"].copy(), ref["v_pool"].copy()
     oracle.copy_blocks(kb, vb, pairs[:3])
     assert np.array_equal(bits(k), kb) and np.array_equal(bits(v), vb)
+
+
+@pytest.mark.parametrize("dt,B,D", [("bf16", 16, 128), ("bf16", 8, 64), ("bf16", 32, 256),
+                                    ("f32", 16, 64), ("f32", 32, 128)])
+def test_write_orders_bit_exact(dt, B, D):
+    """pa_write_kv over rows in prefill order (whole blocks, written as
+    tiles), shifted so that blocks straddle the 256-row chunks, reversed,
+    shuffled, and with skipped (-1) slots: the pools equal the oracle's bit
+    for bit."""
+    rng = np.random.default_rng(307_062 + B + D)
+    Hkv, NB, T = 4, 96, 700
+    blocks = rng.permutation(NB)[:-(-T // B)]
+    slots = (blocks[:, None] * B + np.arange(B)[None, :]).reshape(-1)[:T].astype(np.int64)
+    orders = {
+        "prefill": slots,
+        "shifted": np.concatenate([slots[5:], slots[:5]]),
+        "reversed": slots[::-1].copy(),
+        "shuffled": rng.permutation(slots),
+        "holes": np.where(rng.random(T) < 0.05, -1, slots),
+    }
+    if dt == "bf16":
+        kv = rng.integers(0, 1 << 16, size=(2, T, Hkv, D), dtype=np.uint16)
+    else:
+        kv = rng.standard_normal((2, T, Hkv, D)).astype(np.float32).view(np.uint32)
+    spec = types.SimpleNamespace(dtype=dt)
+    for name, sl in orders.items():
+        _say(f"write order {name} {dt} B={B} D={D}")
+        kb, vb = oracle.new_pools(NB, Hkv, B, D, dt)
+        k, v = pools_from_oracle(spec, kb.copy(), vb.copy())
+        oracle.write_kv(kb, vb, kv[0], kv[1], sl, B)
+        key, val = pools_from_oracle(spec, kv[0], kv[1])
+        pa.write_kv(k, v, key, val, dev(sl))
+        torch.cuda.synchronize()
+        assert_pool_equal(spec, k, v, kb, vb)
 
 
 def test_slot_mapping_edge_rows():
