@@ -166,6 +166,31 @@ def copy_calibration(pairs=2048, reps=5):
                                            "write_bytes_per_launch": pairs * 2 * block}}), flush=True)
 
 
+def host_block_manager_timing(w, steps=200):
+    """Host cost of producing one decode step's metadata with the native block
+    manager for this batch: pa_bm_append (slots and copy pairs) plus
+    pa_bm_block_tables (the rows the decode reads), through the Python binding."""
+    import paged_kv_cache_307_amd as pa
+
+    B, S = w.block_size, w.num_seqs
+    grow = -(-steps // B) + 1
+    mb = w.max_blocks_per_seq + grow
+    nb = w.num_blocks + S * grow
+    mgr = pa.BlockManager(nb, B, S, mb, np.random.default_rng(0).permutation(nb))
+    for s in range(S):
+        st, _ = mgr.allocate(s, int(w.context_lens[s]) - 1)
+        assert st == 0
+    seqs = np.arange(S, dtype=np.int32)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st, _, _ = mgr.append(seqs)
+        assert st == 0
+        mgr.block_tables(seqs)
+    us = (time.perf_counter() - t0) * 1e6 / steps
+    return {"us_per_step": round(us, 2), "steps": steps, "batch": S,
+            "calls": "pa_bm_append + pa_bm_block_tables via the Python binding, host only"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +340,7 @@ def main():
             "traffic": measured_traffic(w.name, P, not args.separate_write, shared),
         },
         "cpu_baseline": cpu,
+        "host_block_manager": host_block_manager_timing(w),
     }
     print(json.dumps(rec), flush=True)
 

@@ -75,7 +75,9 @@ enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent sizes      */
   PA_ERR_UNSUPPORTED = -2, /* a head_dim / block_size / dtype / group size not built */
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required            */
-  PA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed            */
+  PA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed            */
+  PA_ERR_NO_BLOCKS = -5,   /* block manager: not enough free blocks (nothing changed) */
+  PA_ERR_STATE = -6        /* block manager: sequence live/idle state does not allow it */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };

@@ -26,3 +26,9 @@ from .binding import (  # noqa: F401
     status_string,
     write_kv,
 )
+from .block_manager import (  # noqa: F401
+    EXPORTED_BM,
+    PA_ERR_NO_BLOCKS,
+    PA_ERR_STATE,
+    BlockManager,
+)

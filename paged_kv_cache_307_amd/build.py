@@ -2,9 +2,11 @@
 
     python -m paged_kv_cache_307_amd.build
 
-Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` in
-parallel, then linked into ``paged_kv_cache_307_amd/libpa.so``.  Packed fp32
-instructions are disabled for every device compilation.
+Each ``csrc/*.hip`` file is compiled by hipcc, and each host-only
+``csrc/*.cpp`` file (the block manager) by the host C++ compiler, to an object
+in ``_build/`` in parallel; the objects are linked into
+``paged_kv_cache_307_amd/libpa.so``.  Packed fp32 instructions are disabled
+for every device compilation.
 """
 
 from __future__ import annotations
@@ -22,6 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
 SOURCES = ["api.hip", "cache_ops.hip", "decode_mfma.hip", "decode_simt.hip", "decode_merge.hip"]
+HOST_SOURCES = ["block_manager.cpp"]
 ARCH = "gfx950"
 
 
@@ -39,6 +42,17 @@ def hipcc() -> str:
 SOURCE_FLAGS = {
     "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
+
+
+def host_cxx() -> str:
+    for cand in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if cand:
+            return cand
+    raise RuntimeError("no host C++ compiler found (set CXX)")
+
+
+def host_flags() -> list:
+    return ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
 def compile_flags() -> list:
@@ -68,6 +82,9 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         jobs.append((obj, [cc, *compile_flags(), *SOURCE_FLAGS.get(src, []), "-c",
                            os.path.join(CSRC, src), "-o", obj]))
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src.replace(".cpp", ".o"))
+        jobs.append((obj, [host_cxx(), *host_flags(), "-c", os.path.join(CSRC, src), "-o", obj]))
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
         for out in ex.map(lambda j: _run(j[1]), jobs):

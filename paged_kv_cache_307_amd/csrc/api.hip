@@ -228,6 +228,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: shape or dtype not supported";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch failed";
+    case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free KV blocks";
+    case PA_ERR_STATE: return "PA_ERR_STATE: sequence is not in the required live/idle state";
     default: return "unknown status";
   }
 }

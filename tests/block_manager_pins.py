@@ -130,6 +130,11 @@ class World:
         assert nfree == sum(1 for r in refs if r == 0), "free count differs from unreferenced blocks"
 
 
+def _rows(m, seqs):
+    rows, lens = m.block_tables(seqs)
+    return [list(map(int, r)) for r in rows], list(map(int, lens))
+
+
 def _world(make, NB, B, S, MB, free_order=None):
     return World(make(NB, B, S, MB, free_order), NB, B, S, MB)
 
@@ -146,7 +151,7 @@ def check_forty_token_table(make):
     w = _world(make, 32, B, 4, 8, order)
     st, slots = w.allocate(0, 40)
     assert st == OK
-    rows, lens = w.m.block_tables([0])
+    rows, lens = _rows(w.m, [0])
     assert list(rows[0][:3]) == g["printed"]["forty_tokens"]["block_table"]
     assert lens[0] == 40 and list(rows[0][3:]) == [-1] * 5
     for pos, slot in g["derived"]["forty_token_slots"].items():
@@ -161,7 +166,7 @@ def check_seventeen_tokens_tail_first(make):
     B = g["printed"]["block_size"]
     w = _world(make, 8, B, 2, 8)
     assert w.allocate(0, 17)[0] == OK
-    rows, _ = w.m.block_tables([0])
+    rows, _ = _rows(w.m, [0])
     nblk = sum(1 for b in rows[0] if b != -1)
     assert nblk == g["printed"]["seventeen_tokens"]["num_blocks"]
     assert 17 - (nblk - 1) * B == g["printed"]["seventeen_tokens"]["tokens_in_last_block"]
@@ -186,14 +191,14 @@ def check_fork_then_copy_on_write(make):
     w = _world(make, 16, 16, 4, 4)
     assert w.allocate(0, 20)[0] == OK
     assert w.fork(0, 1) == OK
-    rows, _ = w.m.block_tables([0, 1])
+    rows, _ = _rows(w.m, [0, 1])
     assert list(rows[0]) == list(rows[1])
     assert all(w.m.ref_count(b) == 2 for b in rows[0] if b != -1)
     w.verify()
     assert w.m.blocks_needed_to_append([1]) == 1
     st, slots, pairs = w.append([1])
     assert st == OK and len(pairs) == 1 and int(pairs[0][0]) == rows[0][1]
-    after, _ = w.m.block_tables([0, 1])
+    after, _ = _rows(w.m, [0, 1])
     assert list(after[0]) == list(rows[0]), "the other sequence's table changed"
     assert after[1][0] == rows[0][0] and after[1][1] != rows[0][1]
     assert w.m.ref_count(rows[0][0]) == 2 and w.m.ref_count(rows[0][1]) == 1
@@ -210,7 +215,7 @@ def check_fork_at_block_boundary_copies_nothing(make):
     assert w.allocate(0, 32)[0] == OK and w.fork(0, 1) == OK
     st, _, pairs = w.append([1, 0])
     assert st == OK and pairs == []
-    rows, _ = w.m.block_tables([0, 1])
+    rows, _ = _rows(w.m, [0, 1])
     assert rows[0][:2] == rows[1][:2] and rows[0][2] != rows[1][2]
     w.verify()
 

@@ -16,4 +16,5 @@ from .generate import (  # noqa: F401
     shared_prefix,
     mixed_lengths,
     custom,
+    normal_values,
 )

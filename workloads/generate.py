@@ -138,6 +138,12 @@ def _normal(seedseq: np.random.SeedSequence, shape, dtype: str) -> np.ndarray:
     return table[idx].reshape(shape)
 
 
+def normal_values(seed: int, shape, dtype: str) -> np.ndarray:
+    """Seeded N(0, 1) values in workload storage (float32, or bf16 bits as
+    uint16), drawn as described in the module notes."""
+    return _normal(np.random.SeedSequence(seed), shape, dtype)
+
+
 def _streams(seed: int) -> dict:
     children = np.random.SeedSequence(seed).spawn(len(_STREAMS))
     return dict(zip(_STREAMS, children))
