@@ -55,7 +55,8 @@ __all__ = [
     "blocks_needed", "block_token_range", "translate", "slot_of", "slot_mapping",
     "storage_dtype", "to_bits", "widen", "new_pools", "write_kv", "copy_blocks",
     "gather", "attend", "decode", "decode_brute", "attention_unpaged_brute",
-    "contiguous_sequences", "run_step", "tail_waste", "fragmentation_proxy",
+    "contiguous_sequences", "run_step", "prefill", "causal_attention_brute",
+    "contiguous_prefill_sequences", "run_prefill", "tail_waste", "fragmentation_proxy",
     "prealloc_waste", "kv_bytes", "POISON",
 ]
 
@@ -300,6 +301,83 @@ def run_step(w, seqs=None, kv_heads=None):
                  w.scale, w.num_kv_heads, B, w.dtype, seqs=seqs, kv_heads=kv_heads)
     return {"k_pool": k_pool, "v_pool": v_pool, "hist_slots": hist_slots,
             "new_slots": new_slots, "out": out}
+
+
+# --------------------------------------------------------------------------
+# prefill / chunked prefill
+
+def prefill(q_bits, k_pool, v_pool, block_tables, context_lens, query_start, scale: float,
+            num_kv_heads: int, B: int, dtype: str, seqs=None, kv_heads=None) -> np.ndarray:
+    """Causal attention of many query rows per sequence over its paged K/V,
+    fp64 [T, Hq, D].
+
+    Sequence s holds L = context_lens[s] tokens and owns query rows
+    query_start[s] .. query_start[s+1]-1; those n rows are its last n
+    positions, so row i sits at position L - n + i and sees tokens
+    0 .. L - n + i.  [P1 映射逻辑块与物理块: prefill asks for blocks by input
+    length; P2 comparison with FlashAttention and P3 "what PagedAttention
+    changes": paging moves K/V, the formula stays.]  A row whose position is
+    negative sees nothing and gets zeros.  ``seqs`` / ``kv_heads`` restrict
+    the work to a sample; other rows stay NaN.
+    """
+    T, Hq, D = q_bits.shape
+    G = Hq // num_kv_heads
+    q = widen(q_bits, dtype)
+    out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+    S = len(context_lens)
+    for s in (range(S) if seqs is None else seqs):
+        L = int(context_lens[s])
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        n = q1 - q0
+        for g in (range(num_kv_heads) if kv_heads is None else kv_heads):
+            Ks, Vs = gather(k_pool, v_pool, block_tables[s], L, g, B, dtype)
+            for i in range(n):
+                visible = max(L - n + i + 1, 0)
+                out[q0 + i, g * G:(g + 1) * G] = attend(q[q0 + i, g * G:(g + 1) * G],
+                                                        Ks[:visible], Vs[:visible], scale)
+    return out
+
+
+def causal_attention_brute(q, k_seq, v_seq, positions, scale, num_kv_heads):
+    """Textbook causal attention over contiguous K/V, no paging: row i of q
+    [n, Hq, D] sees tokens 0 .. positions[i] of k_seq/v_seq [L, Hkv, D];
+    pure-Python loops through the unpaged brute force."""
+    out = np.zeros(q.shape, dtype=np.float64)
+    for i, p in enumerate(positions):
+        p = int(p)
+        if p < 0:
+            continue
+        out[i] = attention_unpaged_brute(q[i], k_seq[:p + 1], v_seq[:p + 1], scale, num_kv_heads)
+    return out
+
+
+def contiguous_prefill_sequences(w):
+    """Per-sequence contiguous fp64 K/V [L, Hkv, D] from a prefill workload's
+    (sequence, position) rows, no block table involved."""
+    out = []
+    for s in range(w.num_seqs):
+        L = int(w.context_lens[s])
+        k = np.full((L, w.num_kv_heads, w.head_dim), np.nan)
+        v = np.full((L, w.num_kv_heads, w.head_dim), np.nan)
+        sel = np.nonzero(w.kv_seq == s)[0]
+        k[w.kv_pos[sel]] = widen(to_bits(w.key[sel], w.dtype), w.dtype)
+        v[w.kv_pos[sel]] = widen(to_bits(w.value[sel], w.dtype), w.dtype)
+        out.append((k, v))
+    return out
+
+
+def run_prefill(w, seqs=None, kv_heads=None):
+    """One prefill step on a prefill workload: write every cached row at its
+    slot, then attend.  Returns the pools (raw bits), the slots and the fp64
+    output."""
+    B = w.block_size
+    k_pool, v_pool = new_pools(w.num_blocks, w.num_kv_heads, B, w.head_dim, w.dtype)
+    slots = slot_mapping(w.block_tables, w.kv_seq, w.kv_pos, B)
+    write_kv(k_pool, v_pool, to_bits(w.key, w.dtype), to_bits(w.value, w.dtype), slots, B)
+    out = prefill(to_bits(w.q, w.dtype), k_pool, v_pool, w.block_tables, w.context_lens,
+                  w.query_start, w.scale, w.num_kv_heads, B, w.dtype, seqs=seqs,
+                  kv_heads=kv_heads)
+    return {"k_pool": k_pool, "v_pool": v_pool, "slots": slots, "out": out}
 
 
 # --------------------------------------------------------------------------

@@ -17,4 +17,7 @@ from .generate import (  # noqa: F401
     mixed_lengths,
     custom,
     normal_values,
+    PrefillWorkload,
+    prefill,
+    llama3_8b_prefill,
 )

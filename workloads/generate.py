@@ -60,6 +60,9 @@ __all__ = [
     "shared_prefix",
     "mixed_lengths",
     "custom",
+    "PrefillWorkload",
+    "prefill",
+    "llama3_8b_prefill",
 ]
 
 # Quiet-NaN bit patterns used to fill every slot no sequence has written.
@@ -456,3 +459,90 @@ def mixed_lengths(block_size: int = 16, seed: int = 307_005, num_seqs: int = 256
     rows = _allocate_private(lengths, B, NB, np.random.SeedSequence(307_050 + B))
     MB = _blocks_to_hold(max_len, B)
     return _assemble(f"mixed_lengths_B{B}", "bf16", lengths, rows, rows, 64, 8, 128, B, NB, MB, st)
+
+
+# ---------------------------------------------------------------------------
+# prefill / chunked prefill
+
+@dataclasses.dataclass
+class PrefillWorkload:
+    """One prefill step: sequence s holds ``context_lens[s]`` tokens in the
+    cache and brings its last ``query_lens[s]`` positions as query rows
+    ``query_start[s] .. query_start[s+1] - 1``.  ``kv_seq`` / ``kv_pos`` /
+    ``key`` / ``value`` are the rows of every cached token (the chunk's own
+    included), written before the attention."""
+    name: str
+    dtype: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    max_blocks_per_seq: int
+    scale: float
+    context_lens: np.ndarray
+    query_lens: np.ndarray
+    query_start: np.ndarray
+    block_tables: np.ndarray
+    q: np.ndarray
+    kv_seq: np.ndarray
+    kv_pos: np.ndarray
+    key: np.ndarray
+    value: np.ndarray
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.num_seqs else 0
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+
+def prefill(lengths, query_lens, num_heads, num_kv_heads, head_dim, block_size, dtype="bf16",
+            seed=307_300, pool_factor=1.25, name="prefill") -> PrefillWorkload:
+    """Sequences of the given cached lengths (>= 0), each with its last
+    ``query_lens[s]`` positions as query rows, over a shuffled pool."""
+    st = _streams(seed)
+    lengths = np.asarray([int(x) for x in lengths], dtype=np.int32)
+    qlens = np.asarray([int(x) for x in query_lens], dtype=np.int32)
+    if lengths.shape != qlens.shape or (lengths < 0).any() or (qlens < 0).any():
+        raise ValueError("lengths and query_lens: same count, non-negative")
+    B = block_size
+    need = sum(_blocks_to_hold(int(L), B) for L in lengths)
+    NB = max(_pool_size(need, pool_factor), 1)
+    rows = _allocate_private(lengths, B, NB, st["perm"])
+    MB = max(1, max((_blocks_to_hold(int(L), B) for L in lengths), default=1))
+    starts = np.zeros(len(lengths) + 1, dtype=np.int32)
+    starts[1:] = np.cumsum(qlens)
+    T = int(starts[-1])
+    kv_seq = np.concatenate([np.full(int(L), s, np.int32) for s, L in enumerate(lengths)]) \
+        if len(lengths) else np.zeros(0, np.int32)
+    kv_pos = np.concatenate([np.arange(int(L), dtype=np.int32) for L in lengths]) \
+        if len(lengths) else np.zeros(0, np.int32)
+    kv = _normal(st["hist"], (2, len(kv_seq), num_kv_heads, head_dim), dtype)
+    q = _normal(st["q"], (T, num_heads, head_dim), dtype)
+    return PrefillWorkload(
+        name=name, dtype=dtype, num_seqs=len(lengths), num_heads=num_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=B, num_blocks=NB,
+        max_blocks_per_seq=MB, scale=1.0 / math.sqrt(head_dim), context_lens=lengths,
+        query_lens=qlens, query_start=starts, block_tables=_tables_from_rows(rows, MB), q=q,
+        kv_seq=kv_seq, kv_pos=kv_pos, key=kv[0], value=kv[1])
+
+
+def llama3_8b_prefill(seed: int = 307_301, num_seqs: int = 16, chunk: int = 512,
+                      min_len: int = 512, max_len: int = 4096) -> PrefillWorkload:
+    """Chunked prefill of a Llama-3-8B-shaped layer: 16 sequences whose cached
+    lengths are uniform on [512, 4096], each bringing its last 512 positions
+    as one chunk of query rows; 32 query / 8 KV heads, head_dim 128, bf16,
+    B=16, pool 1.25x the blocks needed, shuffled."""
+    st = _streams(seed)
+    lengths = np.random.Generator(np.random.PCG64(st["lengths"])).integers(
+        min_len, max_len, size=num_seqs, endpoint=True)
+    return prefill(lengths, [min(chunk, int(L)) for L in lengths], 32, 8, 128, 16, "bf16",
+                   seed=seed + 1, name="llama3_8b_prefill")
