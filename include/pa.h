@@ -288,6 +288,46 @@ int pa_append_decode_partials(void* out, const void* q, const void* key, const v
                               void* workspace, size_t workspace_bytes, int32_t dtype,
                               int32_t flags, void* stream);
 
+/*
+ * pa_prefill -- paged prefill / chunked-prefill attention: many query tokens
+ * per sequence, causal, over the same paged cache the decode reads.
+ * [P1 映射逻辑块与物理块: prefill asks for blocks by input length and reads
+ *  them through the block table; P2 section 2.1 and section 三: the kernel
+ *  gathers K/V by block and computes softmax(QK^T)V, the formula unchanged
+ *  by paging; P3 PagedAttention 改变了什么: logical_block = t // B, offset =
+ *  t % B.]
+ *
+ *   out           out  [num_query_tokens][num_heads][head_dim], dtype of q
+ *   q             in   [num_query_tokens][num_heads][head_dim]
+ *   k_cache, v_cache in pools in the layout above
+ *   block_tables  in   int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  in   int32 [num_seqs]: L_s, tokens of sequence s in the
+ *                      cache, the query tokens included
+ *   query_start   in   int32 [num_seqs + 1]: sequence s owns query rows
+ *                      query_start[s] .. query_start[s+1] - 1 (n_s rows)
+ *
+ * The n_s query rows of sequence s are its last n_s positions,
+ * L_s - n_s .. L_s - 1, whose K/V the caller has already written (pa_write_kv
+ * at their slots).  Row i attends to tokens 0 .. L_s - n_s + i:
+ *   out[query_start[s] + i][h] = softmax_t(scale * q . K_t) V_t over those
+ * tokens, with query head h reading KV head h / (num_heads / num_kv_heads).
+ * n_s = L_s is a whole prompt, n_s < L_s a chunk after earlier chunks, and
+ * n_s = 1 the decode step.  L_s is clamped as in pa_decode and n_s to the
+ * rows of q.  Only the first max_query_len rows of a sequence are computed
+ * (their positions still count all n_s rows); rows beyond are not written.  A row
+ * whose position is negative (n_s > L_s, a broken precondition) sees no token
+ * and gets zeros.  Any group size is supported.  bf16 runs on matrix cores
+ * (16x16 tiles of (position, head) rows x tokens); fp32 runs one wave per row.
+ * No workspace.  Errors as pa_decode; PA_ERR_UNSUPPORTED when the launch
+ * would exceed the grid limits.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int32_t num_seqs, int32_t num_query_tokens,
+               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+               int32_t max_query_len, float scale, int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

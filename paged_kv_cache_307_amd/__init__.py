@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     kv_cache_shapes,
     library_path,
     load_library,
+    prefill,
     slot_mapping,
     status_string,
     write_kv,

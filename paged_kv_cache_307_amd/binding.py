@@ -24,7 +24,7 @@ _DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
 EXPORTED = (
     "pa_status_string", "pa_slot_mapping", "pa_write_kv", "pa_copy_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partials", "pa_decode_merge",
-    "pa_append_decode", "pa_append_decode_partials",
+    "pa_append_decode", "pa_append_decode_partials", "pa_prefill",
 )
 
 
@@ -64,6 +64,7 @@ def load_library():
                                       [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z,
                                        I, I, P]),
     }
+    sig["pa_prefill"] = (ctypes.c_int, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P])
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
@@ -309,4 +310,30 @@ def append_decode_partials(q, key, value, k_cache, v_cache, block_tables, contex
         int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(q), _flags(shared_blocks),
         _stream(stream))
     _check(st, "pa_append_decode_partials")
+    return out
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, max_context_len,
+            max_query_len, scale, out=None, stream=None):
+    """Causal attention of each sequence's query rows (its last n positions,
+    rows query_start[s] .. query_start[s+1]-1 of q [T, Hq, D]) over its paged
+    K/V; the rows' own K/V must already be in the cache."""
+    nb, hkv, b, d = _cache_dims(k_cache, v_cache)
+    _cuda_contig("q", q, k_cache.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    _cuda_contig("out", out, k_cache.dtype)
+    _cuda_contig("block_tables", block_tables, torch.int32)
+    _cuda_contig("context_lens", context_lens, torch.int32)
+    _cuda_contig("query_start", query_start, torch.int32)
+    _need(q.dim() == 3 and q.shape[2] == d, "q must be [T, Hq, D]")
+    _need(tuple(out.shape) == tuple(q.shape), "out must match q")
+    s = context_lens.numel()
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == s, "block_tables must be [S, MB]")
+    _need(query_start.numel() == s + 1, "query_start must be [S + 1]")
+    st = load_library().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), s, q.shape[0], q.shape[1], hkv, d, b, nb, block_tables.shape[1],
+        int(max_context_len), int(max_query_len), float(scale), _dtype_code(q), _stream(stream))
+    _check(st, "pa_prefill")
     return out

@@ -23,7 +23,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
-SOURCES = ["api.hip", "cache_ops.hip", "decode_mfma.hip", "decode_simt.hip", "decode_merge.hip"]
+SOURCES = ["api.hip", "cache_ops.hip", "decode_mfma.hip", "decode_simt.hip", "decode_merge.hip",
+           "prefill.hip"]
 HOST_SOURCES = ["block_manager.cpp"]
 ARCH = "gfx950"
 

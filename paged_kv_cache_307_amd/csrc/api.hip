@@ -370,6 +370,58 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   return status_of(e);
 }
 
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens,
+               const int32_t* query_start, int32_t num_seqs, int32_t num_query_tokens,
+               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+               int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+               int32_t max_query_len, float scale, int32_t dtype, void* stream) {
+  if (num_seqs < 0 || num_query_tokens < 0 || num_heads < 1 || num_kv_heads < 1 ||
+      num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0 || max_query_len < 0)
+    return PA_ERR_INVALID_ARG;
+  if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (elem_bytes_of(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return PA_ERR_INVALID_ARG;
+  const int32_t group = num_heads / num_kv_heads;
+  const bool bf16 = dtype == PA_DTYPE_BF16;
+  pa::PrefillArgs a{};
+  if (bf16) {
+    const int64_t row_groups = (int64_t(max_query_len) * group + 63) / 64;
+    const int64_t work = row_groups * num_kv_heads * num_seqs;
+    if (work > 0x7FFFFFF8) return PA_ERR_UNSUPPORTED;
+    a.row_groups = int32_t(row_groups);
+    a.work = int32_t(work);
+  } else if (num_heads > 65535 || num_seqs > 65535) {
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (int64_t(num_query_tokens) * num_heads * head_dim > (int64_t(1) << 40)) return PA_ERR_UNSUPPORTED;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_query_tokens = num_query_tokens;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = int32_t(effective_max_len(max_context_len, max_blocks_per_seq, block_size));
+  a.max_query_len = max_query_len;
+  a.scale = scale;
+  a.scale_log2e = scale * 1.4426950408889634f;
+  return status_of(pa::launch_prefill(a, head_dim, block_size, bf16, static_cast<hipStream_t>(stream)));
+}
+
 int pa_append_decode_partials(void* out, const void* q, const void* key, const void* value,
                               void* k_cache, void* v_cache, const int32_t* block_tables,
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

@@ -38,6 +38,30 @@ struct DecodeArgs {
   float scale_log2e;          // scale * log2(e)
 };
 
+// Arguments of one prefill launch.
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;  // [num_seqs + 1] first query row of each sequence
+  int32_t num_seqs;
+  int32_t num_query_tokens;    // rows of q and out
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;               // num_heads / num_kv_heads
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;     // clamp for context_lens
+  int32_t max_query_len;       // clamp for query rows per sequence
+  int32_t row_groups;          // bf16: ceil(max_query_len * group / 64)
+  int32_t work;                // bf16: num_seqs * num_kv_heads * row_groups
+  float scale;
+  float scale_log2e;
+};
+
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Floats in one split-KV record: o[G][D], m[G], l[G], the launch epoch
@@ -90,6 +114,8 @@ int decode_workers_bf16_mfma(int head_dim, int block_size);
 int decode_workers_simt(int head_dim, bool bf16);
 hipError_t launch_decode_simt(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
                               hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16,
+                          hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
                                hipStream_t stream);
 

@@ -1,0 +1,382 @@
+// Paged prefill / chunked-prefill attention on gfx950.
+//
+// What is computed: sequence s holds L_s tokens in its paged K/V (token t in
+// physical block block_table[s][t / B] at offset t % B -- "PagedAttention学习笔记"
+// section 2.1; "KV cache 显存管理", PagedAttention 改变了什么) and brings n_s
+// query tokens, its last n_s positions L_s - n_s .. L_s - 1, whose K/V are
+// already in the cache (written through their slots first).  Query row i of
+// the sequence attends causally: softmax over tokens 0 .. L_s - n_s + i of
+// scale * q.k_t, applied to v_t.  A whole prompt is n_s = L_s; a chunk of a
+// long prompt, or several tokens verified at once, is n_s < L_s; n_s = 1 is
+// the decode step.  The pages' prefill asks for blocks by input length
+// ("什么是 PagedAttention？", 映射逻辑块与物理块) and reads history through the
+// same table as decode; only the number of query rows differs.
+//
+// bf16 kernel.  For one (sequence, KV head) the query rows are the pairs
+// (position i, head of the group) in order, i * G + head; a wave takes 16 of
+// them as the 16 columns of the matrix-core tiles
+//
+//   S^T[16 tok x 16 col] = K_tile[16 tok x D] . Q^T[D x 16 col]   (16x16x32 bf16)
+//   O^T[D x 16 col]     += V^T_tile[D x 16 tok] . P^T[16 tok x 16 col] (16x16x16 bf16)
+//
+// with the operand layouts of the decode kernel (lane l: row/column l & 15,
+// group l >> 4; K rows are 16-byte loads from the [B][D] tile, V columns
+// 8-byte loads from the token-innermost [D][B] tile).  Column c sees tokens
+// below its own limit lim_c = L - n + i_c + 1; tiles below the smallest
+// limit of the wave need no mask.  Four waves (64 consecutive rows) form a
+// workgroup and stream the same tiles, so three of the four reads of a tile
+// hit in the cache; the launch order keeps all row groups of one (sequence,
+// KV head) on one XCD (workgroup i runs on XCD i % 8), heaviest (latest
+// positions) first.
+//
+// fp32 kernel.  One wave per (query row, head): lanes hold D / 64 dims each;
+// each token's dot product is reduced across the wave.  It exists for the
+// tight-tolerance parity of the causal logic, not for speed.
+
+#include <math.h>
+
+#include "device_common.h"
+
+namespace pa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kTile = 16;
+constexpr int kRowsPerGroup = kWaves * kTile;
+constexpr float kRescale = 8.0f;  // lazy maximum: weights stay <= 2^8
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
+  float2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// max / sum of x over the four row groups of an MFMA result column (lanes
+// l, l ^ 16, l ^ 32, l ^ 48), via gfx950 lane swaps.
+__device__ __forceinline__ float col_max(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+  auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Sequence s of the launch: clamped length L, its n query rows (positions
+// L - n .. L - 1), the first `rows` of them computed (at most max_query_len),
+// and the index q0 of its first query row.
+struct SeqRows {
+  int L, n, rows, q0;
+};
+
+__device__ __forceinline__ SeqRows seq_rows(const PrefillArgs& a, int s, int B) {
+  SeqRows r;
+  int L = load_ro(a.context_lens, s);
+  L = L < 0 ? 0 : L;
+  L = L > a.max_context_len ? a.max_context_len : L;
+  const int cap = a.max_blocks_per_seq * B;
+  r.L = L > cap ? cap : L;
+  // rows stay inside q / out even if query_start is not a valid prefix sum
+  int q0 = load_ro(a.query_start, s);
+  q0 = q0 < 0 ? 0 : (q0 > a.num_query_tokens ? a.num_query_tokens : q0);
+  int n = load_ro(a.query_start, s + 1) - q0;
+  n = n < 0 ? 0 : n;
+  r.n = n > a.num_query_tokens - q0 ? a.num_query_tokens - q0 : n;
+  r.rows = r.n > a.max_query_len ? a.max_query_len : r.n;
+  r.q0 = q0;
+  return r;
+}
+
+template <int D>
+struct KVTile {
+  uint4 k[D / 32];
+  uint2 v[D / 16];
+  bool bad;
+};
+
+// Loads of the 16-token tile at t0 of KV head kvh (ids of its block(s) in
+// pb0 / pb1; pb1 is the second block of a B = 8 tile).  Out-of-range ids
+// read block 0 and mark the tile bad.
+template <int D, int B>
+__device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a, int pb0, int pb1,
+                                             int kvh, int t0, int lane) {
+  constexpr int64_t kTileBytes = int64_t(B) * D * 2;
+  const int col = lane & 15, grp = lane >> 4;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  const bool bad0 = unsigned(pb0) >= unsigned(a.num_blocks);
+  const bool bad1 = unsigned(pb1) >= unsigned(a.num_blocks);
+  pb0 = bad0 ? 0 : pb0;
+  pb1 = bad1 ? 0 : pb1;
+  if constexpr (B >= kTile) {
+    const int in_block = t0 % B;
+    const char* kb = kc + (int64_t(pb0) * a.num_kv_heads + kvh) * kTileBytes +
+                     (int64_t(in_block) * D + int64_t(col) * D) * 2 + grp * 16;
+    const char* vb = vc + (int64_t(pb0) * a.num_kv_heads + kvh) * kTileBytes +
+                     (in_block + int64_t(col) * B) * 2 + grp * 8;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) r.k[j] = *reinterpret_cast<const uint4*>(kb + 64 * j);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      r.v[c] = *reinterpret_cast<const uint2*>(vb + int64_t(32) * B * c);
+    r.bad = bad0;
+  } else {
+    const bool k_second = col >= B;
+    const bool v_second = grp >= 2;
+    const int kr = k_second ? col - B : col;
+    const int vt = 4 * grp - (v_second ? B : 0);
+    const char* kb = kc + (int64_t(k_second ? pb1 : pb0) * a.num_kv_heads + kvh) * kTileBytes +
+                     int64_t(kr) * D * 2 + grp * 16;
+    const char* vb = vc + (int64_t(v_second ? pb1 : pb0) * a.num_kv_heads + kvh) * kTileBytes +
+                     (int64_t(col) * B + vt) * 2;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) r.k[j] = *reinterpret_cast<const uint4*>(kb + 64 * j);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      r.v[c] = *reinterpret_cast<const uint2*>(vb + int64_t(32) * B * c);
+    r.bad = v_second ? bad1 : bad0;
+  }
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillArgs a) {
+  constexpr int KSTEPS = D / 32;
+  constexpr int DCH = D / 16;
+  const int G = a.group;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+
+  // XCD-grouped work index: workgroups that run on one XCD take consecutive
+  // work items, i.e. the row groups of one (sequence, KV head).
+  const int per_xcd = gridDim.x / kXcds;
+  const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (w >= a.work) return;
+  const int rg = a.row_groups - 1 - w % a.row_groups;  // latest positions first
+  const int kvh = (w / a.row_groups) % a.num_kv_heads;
+  const int s = w / (a.row_groups * a.num_kv_heads);
+  const SeqRows sr = seq_rows(a, s, B);
+  const int L = wave_uniform(sr.L), n = wave_uniform(sr.n), q0 = wave_uniform(sr.q0);
+  const int nrows = wave_uniform(sr.rows) * G;
+  const int r0 = rg * kRowsPerGroup + wave * kTile;  // first row of this wave
+  if (r0 >= nrows) return;                            // wave-uniform: no barrier below
+  const int r_last = min(r0 + kTile, nrows) - 1;
+  // visible-token limits: column c (row r0 + c, position i = row / G) sees
+  // tokens [0, L - n + i + 1); wave range and the unmasked prefix
+  const int base = L - n + 1;
+  const int t_end = min(L, max(base + r_last / G, 0));
+  const int lim_min = max(base + r0 / G, 0);
+  const int row = r0 + col;
+  const bool col_ok = row < nrows;
+  const int lim = col_ok ? max(base + row / G, 0) : 0;
+  const int qi = row / G, qh = kvh * G + row % G;
+
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  floatx4_t acc[DCH];
+#pragma unroll
+  for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (t_end > 0) {
+    bf16x8_t qop[KSTEPS];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                           (int64_t(q0 + qi) * a.num_heads + qh) * D + 8 * grp;
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * j);
+        qop[j] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
+    const int nblk = (L + B - 1) / B;
+    const int ntile = (t_end + kTile - 1) / kTile;
+    auto ids = [&](int k, int& pb0, int& pb1) {
+      const int lb = k * kTile / B;
+      pb0 = wave_uniform(load_ro(trow, lb));
+      pb1 = pb0;
+      if constexpr (B < kTile) pb1 = lb + 1 < nblk ? wave_uniform(load_ro(trow, lb + 1)) : pb0;
+    };
+
+    auto consume = [&](KVTile<D>& r, int k) {
+      const int t0 = k * kTile;
+      floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
+                                                       qop[j], sacc, 0, 0, 0);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
+      const int tb = t0 + 4 * grp;
+      if (t0 + kTile > lim_min) {  // causal edge (and the tail): per-column limit
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = tb + i < lim ? x[i] : -INFINITY;
+      }
+      if (t0 + kTile > t_end) {  // tokens past the wave's range may be unused slots
+        const int nv = min(max(t_end - tb, 0), 4);
+        const uint32_t mx = (nv >= 1 ? 0x0000FFFFu : 0u) | (nv >= 2 ? 0xFFFF0000u : 0u);
+        const uint32_t my = (nv >= 3 ? 0x0000FFFFu : 0u) | (nv >= 4 ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < DCH; ++c) {
+          r.v[c].x &= mx;
+          r.v[c].y &= my;
+        }
+      }
+      if (r.bad) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
+      }
+      const float tmax = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      if (__any(tmax > m_run + kRescale)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < DCH; ++c) acc[c] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;  // a column that sees nothing yet
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const uint2 pp = make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3]));
+      const short4_t pop = __builtin_bit_cast(short4_t, pp);
+#pragma unroll
+      for (int c = 0; c < DCH; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, r.v[c]),
+                                                           pop, acc[c], 0, 0, 0);
+    };
+
+    // Two register tiles: tile k+1 loads while tile k is consumed.  The load
+    // index is clamped to the last tile so every load is unconditional and
+    // each wait covers exactly the loads before it.
+    KVTile<D> t_a, t_b;
+    int pb0, pb1;
+    ids(0, pb0, pb1);
+    load_kv_tile<D, B>(t_a, a, pb0, pb1, kvh, 0, lane);
+    const int last = ntile - 1;
+    for (int k = 0; k < ntile; k += 2) {
+      int k1 = min(k + 1, last);
+      ids(k1, pb0, pb1);
+      load_kv_tile<D, B>(t_b, a, pb0, pb1, kvh, k1 * kTile, lane);
+      consume(t_a, k);
+      if (k + 1 < ntile) {
+        const int k2 = min(k + 2, last);
+        ids(k2, pb0, pb1);
+        load_kv_tile<D, B>(t_a, a, pb0, pb1, kvh, k2 * kTile, lane);
+        consume(t_b, k + 1);
+      }
+    }
+  }
+
+  const float l_tot = col_sum(l_run);
+  if (col_ok) {
+    const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row that sees no token: zeros
+    uint16_t* o = out + (int64_t(q0 + qi) * a.num_heads + qh) * D + 4 * grp;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c)
+      *reinterpret_cast<uint2*>(o + 16 * c) =
+          make_uint2(pack2_rne(acc[c][0] * inv_l, acc[c][1] * inv_l),
+                     pack2_rne(acc[c][2] * inv_l, acc[c][3] * inv_l));
+  }
+}
+
+// fp32: one wave per (query row, query head), grid over all rows.
+template <int D>
+__global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
+  constexpr int E = D / 64;  // dims per lane: lane + 64 e
+  const int lane = threadIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  const int i = blockIdx.x;
+  const SeqRows sr = seq_rows(a, s, B);
+  if (i >= sr.rows) return;
+  const int kvh = h / a.group;
+  const int lim = min(max(sr.L - sr.n + i + 1, 0), sr.L);
+  const float* qp = static_cast<const float*>(a.q) + (int64_t(sr.q0 + i) * a.num_heads + h) * D;
+  float q[E], acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    q[e] = qp[lane + 64 * e];
+    acc[e] = 0.f;
+  }
+  const float* kc = static_cast<const float*>(a.k_cache);
+  const float* vc = static_cast<const float*>(a.v_cache);
+  const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
+  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < lim; ++t) {
+    int pb = load_ro(trow, t / B);
+    const bool bad = unsigned(pb) >= unsigned(a.num_blocks);
+    pb = bad ? 0 : pb;
+    const int off = t % B;
+    const int64_t tile = (int64_t(pb) * a.num_kv_heads + kvh) * B * D;
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) dot += q[e] * kc[tile + int64_t(off) * D + lane + 64 * e];
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
+    float x = bad ? __builtin_nanf("") : dot * a.scale;
+    const float m_new = fmaxf(m, x);
+    const float alpha = m_new == -INFINITY ? 1.f : expf(m - m_new);
+    const float p = expf(x - m_new);
+    l = l * alpha + p;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      acc[e] = acc[e] * alpha + p * vc[tile + int64_t(lane + 64 * e) * B + off];
+    m = m_new;
+  }
+  float* o = static_cast<float*>(a.out) + (int64_t(sr.q0 + i) * a.num_heads + h) * D;
+  const float inv_l = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[lane + 64 * e] = acc[e] * inv_l;
+}
+
+template <int D>
+hipError_t launch_bf16_d(const PrefillArgs& a, int block_size, hipStream_t stream) {
+  const int64_t groups = (int64_t(a.work) + kXcds - 1) / kXcds * kXcds;
+  const dim3 grid{unsigned(groups)}, block{unsigned(kWaves * 64)};
+  switch (block_size) {
+    case 8: return launch(prefill_bf16_mfma_kernel<D, 8>, grid, block, 0, stream, a);
+    case 16: return launch(prefill_bf16_mfma_kernel<D, 16>, grid, block, 0, stream, a);
+    case 32: return launch(prefill_bf16_mfma_kernel<D, 32>, grid, block, 0, stream, a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16,
+                          hipStream_t stream) {
+  if (bf16) {
+    switch (head_dim) {
+      case 64: return launch_bf16_d<64>(a, block_size, stream);
+      case 128: return launch_bf16_d<128>(a, block_size, stream);
+      case 256: return launch_bf16_d<256>(a, block_size, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  const dim3 grid(unsigned(a.max_query_len), unsigned(a.num_heads), unsigned(a.num_seqs));
+  switch (head_dim) {
+    case 64: return launch(prefill_f32_kernel<64>, grid, dim3(64), 0, stream, a, block_size);
+    case 128: return launch(prefill_f32_kernel<128>, grid, dim3(64), 0, stream, a, block_size);
+    case 256: return launch(prefill_f32_kernel<256>, grid, dim3(64), 0, stream, a, block_size);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

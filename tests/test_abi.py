@@ -175,3 +175,34 @@ def append_call(lib, fn="pa_append_decode", **kw):
 ])
 def test_append_decode_rejects_before_launch(lib, fn, kw, expect):
     assert append_call(lib, fn, **kw) == expect
+
+
+def prefill_call(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=4, T=64, Hq=32, Hkv=8,
+             D=128, B=16, NB=100, MB=64, maxlen=1024, maxq=16, scale=0.088, dtype=BF16)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"],
+                          a["T"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["MB"],
+                          a["maxlen"], a["maxq"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hq=30, Hkv=8), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(T=-1), INVALID),
+    (dict(maxq=-1), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(B=12), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(qs=None), INVALID),
+    (dict(cl=None), INVALID),
+    (dict(out=FAKE_MISALIGNED), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(S=1 << 20, Hq=64, Hkv=64, maxq=1 << 12), UNSUPPORTED),   # grid beyond 2^31 workgroups
+    (dict(S=70000, dtype=F32), UNSUPPORTED),                         # fp32 grid's z limit
+    (dict(S=0), OK),
+    (dict(T=0), OK),
+    (dict(maxq=0, q=None, out=None), OK),
+])
+def test_prefill_rejects_before_launch(lib, kw, expect):
+    assert prefill_call(lib, **kw) == expect
