@@ -74,27 +74,23 @@ constexpr int kWriteChunk = 256;
 // Largest (block, KV head) V tile the write transposes through LDS.
 constexpr int kTileLdsBytes = 32768;
 
-// One wave stores one token row at (block, off), all KV heads: K rows as
-// 16-byte vectors, V one element per (head, dim) at stride block_size.
+// One wave stores KV head h of one token row at (block, off): the K row as
+// 16-byte vectors, V one element per dim at stride block_size.
 template <typename Elem>
-__device__ __forceinline__ void store_row_wave(Elem* __restrict__ k_cache,
-                                               Elem* __restrict__ v_cache,
-                                               const Elem* __restrict__ key_row,
-                                               const Elem* __restrict__ value_row, int64_t block,
-                                               int off, int num_kv_heads, int head_dim,
-                                               int block_size, int lane) {
-  const int row = num_kv_heads * head_dim;
-  const int64_t block_elems = int64_t(row) * block_size;
+__device__ __forceinline__ void store_head_wave(Elem* __restrict__ k_cache,
+                                                Elem* __restrict__ v_cache,
+                                                const Elem* __restrict__ key_row,
+                                                const Elem* __restrict__ value_row, int64_t block,
+                                                int off, int h, int num_kv_heads, int head_dim,
+                                                int block_size, int lane) {
+  const int64_t tile = (block * num_kv_heads + h) * int64_t(block_size) * head_dim;
   constexpr int kVec = 16 / sizeof(Elem);
-  const int dim_vecs = head_dim / kVec;
-  const uint4* src_k = reinterpret_cast<const uint4*>(key_row);
-  for (int v = lane; v < row / kVec; v += 64) {
-    const int h = v / dim_vecs;
-    Elem* dst = k_cache + block * block_elems + (int64_t(h) * block_size + off) * head_dim;
-    reinterpret_cast<uint4*>(dst)[v % dim_vecs] = src_k[v];
-  }
-  Elem* vblk = v_cache + block * block_elems + off;
-  for (int e = lane; e < row; e += 64) vblk[int64_t(e) * block_size] = value_row[e];  // [h][d][off]
+  const uint4* src_k = reinterpret_cast<const uint4*>(key_row + int64_t(h) * head_dim);
+  uint4* dst_k = reinterpret_cast<uint4*>(k_cache + tile + int64_t(off) * head_dim);
+  for (int v = lane; v < head_dim / kVec; v += 64) dst_k[v] = src_k[v];
+  const Elem* src_v = value_row + int64_t(h) * head_dim;
+  Elem* vt = v_cache + tile + off;
+  for (int d = lane; d < head_dim; d += 64) vt[int64_t(d) * block_size] = src_v[d];  // [d][off]
 }
 
 // The write of rows [c0, c0 + n) of a slot mapping, n <= kWriteChunk.
@@ -109,6 +105,9 @@ __device__ __forceinline__ void store_row_wave(Elem* __restrict__ k_cache,
 // this chunk does not fill (and every row when the tile path does not
 // apply) take the element path, one wave per row.  Slots are distinct (the
 // API's precondition), so a block filled here gets no other row anywhere.
+// The grid's second dimension splits the KV heads: workgroup (c, y) writes
+// heads y, y + gridDim.y, ... of chunk c, so a chunk's blocks are written by
+// as many workgroups as there are heads.
 template <typename Elem>
 __global__ __launch_bounds__(kThreads) void write_kv_kernel(
     Elem* __restrict__ k_cache, Elem* __restrict__ v_cache, const Elem* __restrict__ key,
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(
   for (int r = 0; r < n; ++r) {
     if (!s_start[r]) continue;
     const int64_t block = s_slot[r] / B;
-    for (int h = 0; h < num_kv_heads; ++h) {
+    for (int h = blockIdx.y; h < num_kv_heads; h += gridDim.y) {
       const int64_t tile = (block * num_kv_heads + h) * int64_t(B) * head_dim;
       // K: token j's head-h row is contiguous in the source and the tile
       for (int v = t; v < B * dvecs; v += kThreads) {
@@ -195,8 +194,9 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(
     }
     if (in_tile) continue;
     const int64_t row = (c0 + i) * row_elems;
-    store_row_wave(k_cache, v_cache, key + row, value + row, sl / B, int(sl % B), num_kv_heads,
-                   head_dim, B, lane);
+    for (int h = blockIdx.y; h < num_kv_heads; h += gridDim.y)
+      store_head_wave(k_cache, v_cache, key + row, value + row, sl / B, int(sl % B), h,
+                      num_kv_heads, head_dim, B, lane);
   }
 }
 
@@ -255,7 +255,8 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const 
   const int tile_path = v_aligned && (int64_t(block_size) * elem_bytes % 16 == 0) &&
                         int64_t(block_size) * head_dim * elem_bytes <= kTileLdsBytes &&
                         block_size <= kWriteChunk;
-  const dim3 grid(unsigned(ceil_div(num_tokens, kWriteChunk)));
+  const dim3 grid{unsigned(ceil_div(num_tokens, kWriteChunk)),
+                  unsigned(num_kv_heads < 65535 ? num_kv_heads : 65535)};
   if (elem_bytes == 4) {
     return launch(write_kv_kernel<uint32_t>, grid, dim3(kThreads), 0, stream,
                   static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),

@@ -49,7 +49,6 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kTile = 16;
-constexpr int kRowsPerGroup = kWaves * kTile;
 constexpr float kRescale = 8.0f;  // lazy maximum: weights stay <= 2^8
 constexpr int kXcds = 8;
 
@@ -149,10 +148,30 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
   }
 }
 
-template <int D, int B>
+// Block-table window: lane i holds the id of logical block wb + i (clamped to
+// the sequence's last block), so one vector load serves 64 blocks and a
+// tile's id comes from a lane read instead of a scalar load whose latency
+// would sit in front of every tile's loads.
+__device__ __forceinline__ int table_window(const int32_t* trow, int wb, int nblk, int lane) {
+  return trow[min(wb + lane, nblk - 1)];
+}
+
+template <int B>
+__device__ __forceinline__ void tile_ids(int win, int wb, int k, int nblk, int& pb0, int& pb1) {
+  const int lb = k * kTile / B;
+  pb0 = __builtin_amdgcn_readlane(win, lb - wb);
+  pb1 = pb0;
+  if constexpr (B < kTile) pb1 = lb + 1 < nblk ? __builtin_amdgcn_readlane(win, lb + 1 - wb) : pb0;
+}
+
+// NC: 16-row column tiles per wave (each K/V tile feeds NC products of each
+// kind); RING: register tiles in flight (tile k + RING - 1 loads while tile
+// k is consumed).
+template <int D, int B, int NC, int RING>
 __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillArgs a) {
   constexpr int KSTEPS = D / 32;
   constexpr int DCH = D / 16;
+  constexpr int kWaveRows = kTile * NC;
   const int G = a.group;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -170,129 +189,149 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
   const SeqRows sr = seq_rows(a, s, B);
   const int L = wave_uniform(sr.L), n = wave_uniform(sr.n), q0 = wave_uniform(sr.q0);
   const int nrows = wave_uniform(sr.rows) * G;
-  const int r0 = rg * kRowsPerGroup + wave * kTile;  // first row of this wave
-  if (r0 >= nrows) return;                            // wave-uniform: no barrier below
-  const int r_last = min(r0 + kTile, nrows) - 1;
-  // visible-token limits: column c (row r0 + c, position i = row / G) sees
-  // tokens [0, L - n + i + 1); wave range and the unmasked prefix
+  const int r0 = (rg * kWaves + wave) * kWaveRows;  // first row of this wave
+  if (r0 >= nrows) return;                           // wave-uniform: no barrier below
+  const int r_last = min(r0 + kWaveRows, nrows) - 1;
+  // visible-token limits: row r (position i = r / G) sees tokens
+  // [0, L - n + i + 1); the wave's range and its unmasked prefix
   const int base = L - n + 1;
   const int t_end = min(L, max(base + r_last / G, 0));
   const int lim_min = max(base + r0 / G, 0);
-  const int row = r0 + col;
-  const bool col_ok = row < nrows;
-  const int lim = col_ok ? max(base + row / G, 0) : 0;
-  const int qi = row / G, qh = kvh * G + row % G;
-
-  uint16_t* out = static_cast<uint16_t*>(a.out);
-  floatx4_t acc[DCH];
+  int lim[NC], qi[NC], qh[NC];
+  bool col_ok[NC];
 #pragma unroll
-  for (int c = 0; c < DCH; ++c) acc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int c = 0; c < NC; ++c) {
+    const int row = r0 + c * kTile + col;
+    col_ok[c] = row < nrows;
+    lim[c] = col_ok[c] ? max(base + row / G, 0) : 0;
+    qi[c] = row / G;
+    qh[c] = kvh * G + row % G;
+  }
+
+  floatx4_t acc[NC][DCH];
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+#pragma unroll
+    for (int d = 0; d < DCH; ++d) acc[c][d] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+  }
 
   if (t_end > 0) {
-    bf16x8_t qop[KSTEPS];
-    {
+    bf16x8_t qop[NC][KSTEPS];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                           (int64_t(q0 + qi) * a.num_heads + qh) * D + 8 * grp;
+                           (int64_t(q0 + qi[c]) * a.num_heads + qh[c]) * D + 8 * grp;
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j) {
         uint4 v = make_uint4(0, 0, 0, 0);
-        if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * j);
-        qop[j] = __builtin_bit_cast(bf16x8_t, v);
+        if (col_ok[c]) v = *reinterpret_cast<const uint4*>(qp + 32 * j);
+        qop[c][j] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
     const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
     const int nblk = (L + B - 1) / B;
     const int ntile = (t_end + kTile - 1) / kTile;
-    auto ids = [&](int k, int& pb0, int& pb1) {
-      const int lb = k * kTile / B;
-      pb0 = wave_uniform(load_ro(trow, lb));
-      pb1 = pb0;
-      if constexpr (B < kTile) pb1 = lb + 1 < nblk ? wave_uniform(load_ro(trow, lb + 1)) : pb0;
-    };
+    const int last = ntile - 1;
 
     auto consume = [&](KVTile<D>& r, int k) {
       const int t0 = k * kTile;
-      floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < KSTEPS; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
-                                                       qop[j], sacc, 0, 0, 0);
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
       const int tb = t0 + 4 * grp;
-      if (t0 + kTile > lim_min) {  // causal edge (and the tail): per-column limit
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = tb + i < lim ? x[i] : -INFINITY;
-      }
       if (t0 + kTile > t_end) {  // tokens past the wave's range may be unused slots
         const int nv = min(max(t_end - tb, 0), 4);
         const uint32_t mx = (nv >= 1 ? 0x0000FFFFu : 0u) | (nv >= 2 ? 0xFFFF0000u : 0u);
         const uint32_t my = (nv >= 3 ? 0x0000FFFFu : 0u) | (nv >= 4 ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int c = 0; c < DCH; ++c) {
-          r.v[c].x &= mx;
-          r.v[c].y &= my;
+        for (int d = 0; d < DCH; ++d) {
+          r.v[d].x &= mx;
+          r.v[d].y &= my;
         }
       }
-      if (r.bad) {
+      const bool edge = t0 + kTile > lim_min;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
+      for (int c = 0; c < NC; ++c) {
+        floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KSTEPS; ++j)
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
+                                                         qop[c][j], sacc, 0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
+        if (edge) {  // causal edge (and the tail): per-column limit
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = tb + i < lim[c] ? x[i] : -INFINITY;
+        }
+        if (r.bad) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
+        }
+        const float tmax = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+        if (__any(tmax > m_run[c] + kRescale)) {
+          const float m_new = fmaxf(m_run[c], tmax);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
+          l_run[c] *= alpha;
+#pragma unroll
+          for (int d = 0; d < DCH; ++d) acc[c][d] *= alpha;
+          m_run[c] = m_new;
+        }
+        const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];  // sees nothing yet
+        float pr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+        l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        const uint2 pp = make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3]));
+        const short4_t pop = __builtin_bit_cast(short4_t, pp);
+#pragma unroll
+        for (int d = 0; d < DCH; ++d)
+          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(short4_t, r.v[d]), pop, acc[c][d], 0, 0, 0);
       }
-      const float tmax = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-      if (__any(tmax > m_run + kRescale)) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int c = 0; c < DCH; ++c) acc[c] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;  // a column that sees nothing yet
-      float pr[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
-      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      const uint2 pp = make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3]));
-      const short4_t pop = __builtin_bit_cast(short4_t, pp);
-#pragma unroll
-      for (int c = 0; c < DCH; ++c)
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, r.v[c]),
-                                                           pop, acc[c], 0, 0, 0);
     };
 
-    // Two register tiles: tile k+1 loads while tile k is consumed.  The load
-    // index is clamped to the last tile so every load is unconditional and
-    // each wait covers exactly the loads before it.
-    KVTile<D> t_a, t_b;
-    int pb0, pb1;
-    ids(0, pb0, pb1);
-    load_kv_tile<D, B>(t_a, a, pb0, pb1, kvh, 0, lane);
-    const int last = ntile - 1;
-    for (int k = 0; k < ntile; k += 2) {
-      int k1 = min(k + 1, last);
-      ids(k1, pb0, pb1);
-      load_kv_tile<D, B>(t_b, a, pb0, pb1, kvh, k1 * kTile, lane);
-      consume(t_a, k);
-      if (k + 1 < ntile) {
-        const int k2 = min(k + 2, last);
-        ids(k2, pb0, pb1);
-        load_kv_tile<D, B>(t_a, a, pb0, pb1, kvh, k2 * kTile, lane);
-        consume(t_b, k + 1);
+    // Ring of RING register tiles; every load is issued unconditionally (the
+    // index clamped to the last tile) so each wait covers exactly the loads
+    // before it.  Block ids come from a table window reloaded when a tile's
+    // blocks leave it.
+    KVTile<D> ring[RING];
+    int wb = 0;
+    int win = table_window(trow, 0, nblk, lane);
+    auto issue = [&](KVTile<D>& r, int k) {
+      k = min(k, last);
+      if (k * kTile / B - wb + (B < kTile ? 1 : 0) >= 64) {  // wave-uniform
+        wb = k * kTile / B;
+        win = table_window(trow, wb, nblk, lane);
+      }
+      int pb0, pb1;
+      tile_ids<B>(win, wb, k, nblk, pb0, pb1);
+      load_kv_tile<D, B>(r, a, pb0, pb1, kvh, k * kTile, lane);
+    };
+#pragma unroll
+    for (int d = 0; d < RING - 1; ++d) issue(ring[d], d);
+    for (int k = 0; k < ntile; k += RING) {
+#pragma unroll
+      for (int d = 0; d < RING; ++d) {
+        issue(ring[(d + RING - 1) % RING], k + d + RING - 1);
+        if (k + d < ntile) consume(ring[d], k + d);
       }
     }
   }
 
-  const float l_tot = col_sum(l_run);
-  if (col_ok) {
-    const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row that sees no token: zeros
-    uint16_t* o = out + (int64_t(q0 + qi) * a.num_heads + qh) * D + 4 * grp;
 #pragma unroll
-    for (int c = 0; c < DCH; ++c)
-      *reinterpret_cast<uint2*>(o + 16 * c) =
-          make_uint2(pack2_rne(acc[c][0] * inv_l, acc[c][1] * inv_l),
-                     pack2_rne(acc[c][2] * inv_l, acc[c][3] * inv_l));
+  for (int c = 0; c < NC; ++c) {
+    const float l_tot = col_sum(l_run[c]);
+    if (col_ok[c]) {
+      const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row that sees no token: zeros
+      uint16_t* o = static_cast<uint16_t*>(a.out) +
+                    (int64_t(q0 + qi[c]) * a.num_heads + qh[c]) * D + 4 * grp;
+#pragma unroll
+      for (int d = 0; d < DCH; ++d)
+        *reinterpret_cast<uint2*>(o + 16 * d) =
+            make_uint2(pack2_rne(acc[c][d][0] * inv_l, acc[c][d][1] * inv_l),
+                       pack2_rne(acc[c][d][2] * inv_l, acc[c][d][3] * inv_l));
+    }
   }
 }
 
@@ -346,23 +385,47 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
   for (int e = 0; e < E; ++e) o[lane + 64 * e] = acc[e] * inv_l;
 }
 
+// Column tiles per wave of the bf16 kernel for head_dim D (the larger D, the
+// more registers a column tile holds).  Measured on the 16-sequence,
+// 512-token-chunk layer at D = 128: 1 tile per wave 2.02 ms, 2 tiles 1.14 ms,
+// 4 tiles 0.98 ms; two or three register tiles in the ring made no
+// difference.
 template <int D>
-hipError_t launch_bf16_d(const PrefillArgs& a, int block_size, hipStream_t stream) {
+constexpr int prefill_nc() { return D >= 256 ? 2 : 4; }
+constexpr int kPrefillRing = 2;
+
+template <int D>
+hipError_t launch_bf16_d(PrefillArgs a, int block_size, hipStream_t stream) {
+  constexpr int NC = prefill_nc<D>();
+  constexpr int RING = kPrefillRing;
   const int64_t groups = (int64_t(a.work) + kXcds - 1) / kXcds * kXcds;
   const dim3 grid{unsigned(groups)}, block{unsigned(kWaves * 64)};
   switch (block_size) {
-    case 8: return launch(prefill_bf16_mfma_kernel<D, 8>, grid, block, 0, stream, a);
-    case 16: return launch(prefill_bf16_mfma_kernel<D, 16>, grid, block, 0, stream, a);
-    case 32: return launch(prefill_bf16_mfma_kernel<D, 32>, grid, block, 0, stream, a);
+    case 8: return launch(prefill_bf16_mfma_kernel<D, 8, NC, RING>, grid, block, 0, stream, a);
+    case 16: return launch(prefill_bf16_mfma_kernel<D, 16, NC, RING>, grid, block, 0, stream, a);
+    case 32: return launch(prefill_bf16_mfma_kernel<D, 32, NC, RING>, grid, block, 0, stream, a);
     default: return hipErrorInvalidValue;
+  }
+}
+
+// Rows of one workgroup of the bf16 kernel.
+int prefill_group_rows(int head_dim) {
+  switch (head_dim) {
+    case 64: return kWaves * kTile * prefill_nc<64>();
+    case 128: return kWaves * kTile * prefill_nc<128>();
+    default: return kWaves * kTile * prefill_nc<256>();
   }
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16,
+hipError_t launch_prefill(const PrefillArgs& a0, int head_dim, int block_size, bool bf16,
                           hipStream_t stream) {
+  PrefillArgs a = a0;
   if (bf16) {
+    const int64_t rows = prefill_group_rows(head_dim);
+    a.row_groups = int32_t((int64_t(a.max_query_len) * a.group + rows - 1) / rows);
+    a.work = a.row_groups * a.num_kv_heads * a.num_seqs;
     switch (head_dim) {
       case 64: return launch_bf16_d<64>(a, block_size, stream);
       case 128: return launch_bf16_d<128>(a, block_size, stream);
