@@ -56,7 +56,9 @@ __all__ = [
     "storage_dtype", "to_bits", "widen", "new_pools", "write_kv", "copy_blocks",
     "gather", "attend", "decode", "decode_brute", "attention_unpaged_brute",
     "contiguous_sequences", "run_step", "prefill", "causal_attention_brute",
-    "contiguous_prefill_sequences", "run_prefill", "tail_waste", "fragmentation_proxy",
+    "contiguous_prefill_sequences", "run_prefill", "attend_lse", "prefill_lse", "merge_states",
+    "cp_owner", "cp_local_offset", "cp_slot_mapping", "cp_context_len",
+    "map_to_kernel_blocks", "tail_waste", "fragmentation_proxy",
     "prealloc_waste", "kv_bytes", "POISON",
 ]
 
@@ -378,6 +380,118 @@ def run_prefill(w, seqs=None, kv_heads=None):
                   w.query_start, w.scale, w.num_kv_heads, B, w.dtype, seqs=seqs,
                   kv_heads=kv_heads)
     return {"k_pool": k_pool, "v_pool": v_pool, "slots": slots, "out": out}
+
+
+# --------------------------------------------------------------------------
+# context parallelism: rank-interleaved tokens, per-rank partials, merge
+#
+# [P2 BlockTable walkthrough]: under decode / prefill context parallelism the
+# slot mapping uses a virtual block size and a mask, writing -1 for entries a
+# rank does not own; when the allocator's block size differs from the one
+# the kernel needs, each allocator block is split into several kernel
+# blocks.  The pages give no formula for ownership.  Reading taken: W ranks
+# share one block table; a virtual block of B * W tokens maps to table entry
+# table[p // (B * W)] on every rank (each rank has its own pool); inside it,
+# runs of I tokens (the interleave, I dividing B) go to the ranks in turn,
+# and a rank packs the runs it owns in order into its B slots of the block.
+
+def cp_owner(p: int, B: int, W: int, I: int) -> int:
+    """Rank owning logical token p."""
+    return (p % (B * W)) // I % W
+
+
+def cp_local_offset(p: int, B: int, W: int, I: int) -> int:
+    """Offset of token p inside its owner's block."""
+    vo = p % (B * W)
+    return vo // (I * W) * I + vo % I
+
+
+def cp_slot_mapping(block_tables, seq_idx, positions, B: int, W: int, rank: int,
+                    I: int = 1) -> np.ndarray:
+    """Slots of rank ``rank``: table[p // (B W)] * B + local offset for the
+    tokens it owns, -1 for the others."""
+    out = np.full(len(positions), -1, dtype=np.int64)
+    for i, (s, p) in enumerate(zip(seq_idx, positions)):
+        s, p = int(s), int(p)
+        if cp_owner(p, B, W, I) != rank:
+            continue
+        out[i] = int(block_tables[s][p // (B * W)]) * B + cp_local_offset(p, B, W, I)
+    return out
+
+
+def cp_context_len(L: int, B: int, W: int, rank: int, I: int = 1) -> int:
+    """Tokens of a length-L sequence that rank ``rank`` holds (counted one
+    by one)."""
+    return sum(1 for p in range(L) if cp_owner(p, B, W, I) == rank)
+
+
+def attend_lse(q_rows, Ks, Vs, scale):
+    """softmax(q K^T scale) V and the natural log of sum_t exp(q.k_t scale)
+    per row; an empty K gives zeros and -inf."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    if Ks.shape[0] == 0:
+        return (np.zeros((q_rows.shape[0], Vs.shape[1])),
+                np.full(q_rows.shape[0], -np.inf))
+    logits = (q_rows @ Ks.T) * scale
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    den = w.sum(axis=1, keepdims=True)
+    return (w @ Vs) / den, (m + np.log(den))[:, 0]
+
+
+def prefill_lse(q_bits, k_pool, v_pool, block_tables, context_lens, query_start, scale,
+                num_kv_heads, B, dtype):
+    """``prefill`` plus each row's log-sum-exp, fp64 [T, Hq, D] and [T, Hq]."""
+    T, Hq, D = q_bits.shape
+    G = Hq // num_kv_heads
+    q = widen(q_bits, dtype)
+    out = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    for s in range(len(context_lens)):
+        L = int(context_lens[s])
+        q0, q1 = int(query_start[s]), int(query_start[s + 1])
+        n = q1 - q0
+        for g in range(num_kv_heads):
+            Ks, Vs = gather(k_pool, v_pool, block_tables[s], L, g, B, dtype)
+            for i in range(n):
+                visible = max(L - n + i + 1, 0)
+                o, l = attend_lse(q[q0 + i, g * G:(g + 1) * G], Ks[:visible], Vs[:visible], scale)
+                out[q0 + i, g * G:(g + 1) * G] = o
+                lse[q0 + i, g * G:(g + 1) * G] = l
+    return out, lse
+
+
+def merge_states(outs, lses):
+    """Combine partial attentions over disjoint token sets: with M the largest
+    log-sum-exp, out = sum_w e^(lse_w - M) o_w / sum_w e^(lse_w - M) (the
+    log-sum-exp identity).  outs [W, ..., D], lses [W, ...]; rows whose every
+    lse is -inf give zeros and -inf."""
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    M = lses.max(axis=0)
+    Ms = np.where(np.isfinite(M), M, 0.0)
+    w = np.exp(lses - Ms[None])
+    den = w.sum(axis=0)
+    num = (w[..., None] * outs).sum(axis=0)
+    safe = np.where(den > 0, den, 1.0)
+    out = np.where((den > 0)[..., None], num / safe[..., None], 0.0)
+    lse = np.where(den > 0, Ms + np.log(safe), -np.inf)
+    return out, lse
+
+
+def map_to_kernel_blocks(manager_tables, k: int) -> np.ndarray:
+    """Allocator block b of k * B_kernel tokens is kernel blocks b*k .. b*k+k-1:
+    row [i] -> row [i*k + j] = table[i] * k + j (-1 stays -1)."""
+    mt = np.asarray(manager_tables)
+    rows, mb = mt.shape
+    kt = np.full((rows, mb * k), -1, dtype=np.int32)
+    for r in range(rows):
+        for i in range(mb):
+            if mt[r, i] < 0:
+                continue
+            for j in range(k):
+                kt[r, i * k + j] = mt[r, i] * k + j
+    return kt
 
 
 # --------------------------------------------------------------------------
