@@ -298,6 +298,10 @@ int pa_append_decode_partials(void* out, const void* q, const void* key, const v
  *  t % B.]
  *
  *   out           out  [num_query_tokens][num_heads][head_dim], dtype of q
+ *   lse           out  fp32 [num_query_tokens][num_heads], or NULL: the natural
+ *                      log of sum_t exp(scale * q . K_t) over the tokens the
+ *                      row sees (-inf for a row that sees none) -- what
+ *                      pa_merge_states needs to combine partial results
  *   q             in   [num_query_tokens][num_heads][head_dim]
  *   k_cache, v_cache in pools in the layout above
  *   block_tables  in   int32 [num_seqs][max_blocks_per_seq]
@@ -321,12 +325,89 @@ int pa_append_decode_partials(void* out, const void* q, const void* key, const v
  * No workspace.  Errors as pa_decode; PA_ERR_UNSUPPORTED when the launch
  * would exceed the grid limits.
  */
-int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+int pa_prefill(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start, int32_t num_seqs, int32_t num_query_tokens,
                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                int32_t max_query_len, float scale, int32_t dtype, void* stream);
+
+/*
+ * Context parallelism.
+ * [P2 BlockTable walkthrough: under decode / prefill context parallelism the
+ *  slot mapping uses a virtual block size and a mask, and writes -1 for the
+ *  entries a rank does not own.]
+ *
+ * The pages give no ownership formula; the one used here: cp_world ranks
+ * share one block table and each has its own pool.  Token p lies in virtual
+ * block p / (block_size * cp_world), i.e. table entry
+ * block_tables[s][p / (block_size * cp_world)] on every rank.  Inside the
+ * virtual block, runs of `interleave` tokens (a divisor of block_size) go to
+ * ranks 0 .. cp_world-1 in turn, and a rank packs the runs it owns into the
+ * block_size slots of its copy of the block, in order.  A rank's tokens thus
+ * form an ordinary paged sequence in its own pool, whose length
+ * pa_cp_context_lens gives: any decode or prefill call attends over it, and
+ * pa_merge_states combines the ranks' results (each with its log-sum-exp).
+ * cp_world = 1 is the plain mapping.  Exchanging the partial results between
+ * GPUs is the caller's (one all-gather of out and lse per step).
+ */
+
+/*
+ * pa_cp_slot_mapping -- rank cp_rank's slot of each (sequence, position)
+ * row: block_tables[s][p / (B * W)] * B + local offset for tokens the rank
+ * owns, -1 for the others and for rows outside the table (as
+ * pa_slot_mapping).  Arguments as pa_slot_mapping plus cp_world >= 1,
+ * 0 <= cp_rank < cp_world, interleave >= 1 dividing block_size.
+ */
+int pa_cp_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                       const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t cp_world, int32_t cp_rank, int32_t interleave, void* stream);
+
+/*
+ * pa_cp_context_lens -- tokens rank cp_rank holds of each sequence:
+ *   local_lens  out  int32 [num_seqs]
+ *   context_lens in  int32 [num_seqs] (negative counts as 0)
+ */
+int pa_cp_context_lens(int32_t* local_lens, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t block_size, int32_t cp_world, int32_t cp_rank, int32_t interleave,
+                       void* stream);
+
+/*
+ * pa_merge_states -- combine partial attention results over disjoint token
+ * sets (context-parallel ranks, or any split of a sequence's tokens) with
+ * the log-sum-exp identity:
+ *   out[r] = sum_w e^(lse_w[r] - M) states_w[r] / sum_w e^(lse_w[r] - M),
+ *   out_lse[r] = M + ln sum_w e^(lse_w[r] - M),  M = max_w lse_w[r].
+ *   out         out  [num_rows][head_dim], dtype
+ *   out_lse     out  fp32 [num_rows], or NULL
+ *   states      in   [num_states][num_rows][head_dim], dtype
+ *   state_lses  in   fp32 [num_states][num_rows]
+ * A row of a decode or prefill output is one (token, head): num_rows =
+ * tokens * heads.  A state whose lse is -inf (no tokens) is ignored; a row
+ * whose every lse is -inf gets zeros and -inf; a NaN lse makes the row NaN.
+ * head_dim must be a multiple of 4; out and states aligned to 4 elements.
+ */
+int pa_merge_states(void* out, float* out_lse, const void* states, const float* state_lses,
+                    int32_t num_states, int32_t num_rows, int32_t head_dim, int32_t dtype,
+                    void* stream);
+
+/*
+ * pa_map_to_kernel_blocks -- tables for the kernel when the allocator's
+ * block holds k = kernel_blocks_per_block kernel blocks.
+ * [P2 BlockTable walkthrough: when the allocator's block size differs from
+ *  the one the kernel needs, each allocator block is split into several
+ *  kernel blocks.]
+ *   kernel_tables  out int32 [num_rows][max_blocks_per_row * k]
+ *   manager_tables in  int32 [num_rows][max_blocks_per_row]
+ * Entry i * k + j = manager_tables[i] * k + j (-1 stays -1, and so does an id
+ * whose product overflows int32): the pool is laid out in kernel blocks, and
+ * allocator block b is kernel blocks b*k .. b*k+k-1.  Every token then has
+ * the same slot number through either table (at block sizes k*B and B).
+ */
+int pa_map_to_kernel_blocks(int32_t* kernel_tables, const int32_t* manager_tables,
+                            int32_t num_rows, int32_t max_blocks_per_row,
+                            int32_t kernel_blocks_per_block, void* stream);
 
 #ifdef __cplusplus
 }

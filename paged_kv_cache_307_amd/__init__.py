@@ -23,6 +23,10 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     prefill,
+    cp_slot_mapping,
+    cp_context_lens,
+    merge_states,
+    map_to_kernel_blocks,
     slot_mapping,
     status_string,
     write_kv,

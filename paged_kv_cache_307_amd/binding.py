@@ -24,7 +24,8 @@ _DTYPES = {torch.float32: PA_DTYPE_F32, torch.bfloat16: PA_DTYPE_BF16}
 EXPORTED = (
     "pa_status_string", "pa_slot_mapping", "pa_write_kv", "pa_copy_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partials", "pa_decode_merge",
-    "pa_append_decode", "pa_append_decode_partials", "pa_prefill",
+    "pa_append_decode", "pa_append_decode_partials", "pa_prefill", "pa_cp_slot_mapping",
+    "pa_cp_context_lens", "pa_merge_states", "pa_map_to_kernel_blocks",
 )
 
 
@@ -64,7 +65,12 @@ def load_library():
                                       [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z,
                                        I, I, P]),
     }
-    sig["pa_prefill"] = (ctypes.c_int, [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P])
+    sig["pa_prefill"] = (ctypes.c_int,
+                         [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P])
+    sig["pa_cp_slot_mapping"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, I, I, I, P])
+    sig["pa_cp_context_lens"] = (ctypes.c_int, [P, P, I, I, I, I, I, P])
+    sig["pa_merge_states"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, P])
+    sig["pa_map_to_kernel_blocks"] = (ctypes.c_int, [P, P, I, I, I, P])
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
@@ -314,10 +320,11 @@ def append_decode_partials(q, key, value, k_cache, v_cache, block_tables, contex
 
 
 def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, max_context_len,
-            max_query_len, scale, out=None, stream=None):
+            max_query_len, scale, out=None, lse=None, stream=None):
     """Causal attention of each sequence's query rows (its last n positions,
     rows query_start[s] .. query_start[s+1]-1 of q [T, Hq, D]) over its paged
-    K/V; the rows' own K/V must already be in the cache."""
+    K/V; the rows' own K/V must already be in the cache.  ``lse``: an fp32
+    [T, Hq] tensor that receives each row's log-sum-exp."""
     nb, hkv, b, d = _cache_dims(k_cache, v_cache)
     _cuda_contig("q", q, k_cache.dtype)
     if out is None:
@@ -331,9 +338,82 @@ def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, max_co
     s = context_lens.numel()
     _need(block_tables.dim() == 2 and block_tables.shape[0] == s, "block_tables must be [S, MB]")
     _need(query_start.numel() == s + 1, "query_start must be [S + 1]")
+    if lse is not None:
+        _cuda_contig("lse", lse, torch.float32)
+        _need(tuple(lse.shape) == tuple(q.shape[:2]), "lse must be [T, Hq]")
     st = load_library().pa_prefill(
-        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         _ptr(query_start), s, q.shape[0], q.shape[1], hkv, d, b, nb, block_tables.shape[1],
         int(max_context_len), int(max_query_len), float(scale), _dtype_code(q), _stream(stream))
     _check(st, "pa_prefill")
+    return out
+
+
+def cp_slot_mapping(block_tables, seq_ids, positions, block_size, cp_world, cp_rank, interleave=1,
+                    out=None, stream=None):
+    """int64 slot of each (sequence, position) row on context-parallel rank
+    cp_rank (-1 for tokens other ranks own)."""
+    _cuda_contig("block_tables", block_tables, torch.int32)
+    _cuda_contig("seq_ids", seq_ids, torch.int32)
+    _cuda_contig("positions", positions, torch.int32)
+    n = seq_ids.numel()
+    _need(positions.numel() == n, "seq_ids and positions must have the same length")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int64, device=seq_ids.device)
+    _cuda_contig("out", out, torch.int64)
+    st = load_library().pa_cp_slot_mapping(
+        _ptr(out), _ptr(block_tables), _ptr(seq_ids), _ptr(positions), n, block_tables.shape[0],
+        block_tables.shape[1], int(block_size), int(cp_world), int(cp_rank), int(interleave),
+        _stream(stream))
+    _check(st, "pa_cp_slot_mapping")
+    return out
+
+
+def cp_context_lens(context_lens, block_size, cp_world, cp_rank, interleave=1, out=None,
+                    stream=None):
+    """Tokens of each sequence that context-parallel rank cp_rank holds."""
+    _cuda_contig("context_lens", context_lens, torch.int32)
+    if out is None:
+        out = torch.empty_like(context_lens)
+    _cuda_contig("out", out, torch.int32)
+    st = load_library().pa_cp_context_lens(
+        _ptr(out), _ptr(context_lens), context_lens.numel(), int(block_size), int(cp_world),
+        int(cp_rank), int(interleave), _stream(stream))
+    _check(st, "pa_cp_context_lens")
+    return out
+
+
+def merge_states(states, state_lses, out=None, out_lse=None, stream=None):
+    """Combine partial results states [W, ..., D] with their log-sum-exps
+    [W, ...] (fp32) into out [..., D] (and out_lse [...])."""
+    _cuda_contig("states", states)
+    _cuda_contig("state_lses", state_lses, torch.float32)
+    _need(states.dim() >= 2 and tuple(state_lses.shape) == tuple(states.shape[:-1]),
+          "state_lses must be states' shape without the last dim")
+    w, d = states.shape[0], states.shape[-1]
+    rows = state_lses[0].numel()
+    if out is None:
+        out = torch.empty(states.shape[1:], dtype=states.dtype, device=states.device)
+    _cuda_contig("out", out, states.dtype)
+    if out_lse is not None:
+        _cuda_contig("out_lse", out_lse, torch.float32)
+        _need(out_lse.numel() == rows, "out_lse must hold one value per row")
+    st = load_library().pa_merge_states(_ptr(out), _ptr(out_lse), _ptr(states), _ptr(state_lses),
+                                        w, rows, d, _dtype_code(states), _stream(stream))
+    _check(st, "pa_merge_states")
+    return out
+
+
+def map_to_kernel_blocks(manager_tables, kernel_blocks_per_block, out=None, stream=None):
+    """Kernel block tables [rows, MB * k] from allocator tables [rows, MB]."""
+    _cuda_contig("manager_tables", manager_tables, torch.int32)
+    rows, mb = manager_tables.shape
+    k = int(kernel_blocks_per_block)
+    if out is None:
+        out = torch.empty((rows, mb * k), dtype=torch.int32, device=manager_tables.device)
+    _cuda_contig("out", out, torch.int32)
+    _need(tuple(out.shape) == (rows, mb * k), "out must be [rows, MB * k]")
+    st = load_library().pa_map_to_kernel_blocks(_ptr(out), _ptr(manager_tables), rows, mb, k,
+                                                _stream(stream))
+    _check(st, "pa_map_to_kernel_blocks")
     return out

@@ -24,7 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libpa.so")
 SOURCES = ["api.hip", "cache_ops.hip", "decode_mfma.hip", "decode_simt.hip", "decode_merge.hip",
-           "prefill.hip"]
+           "prefill.hip", "context_parallel.hip"]
 HOST_SOURCES = ["block_manager.cpp"]
 ARCH = "gfx950"
 

@@ -370,7 +370,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   return status_of(e);
 }
 
-int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+int pa_prefill(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, const int32_t* context_lens,
                const int32_t* query_start, int32_t num_seqs, int32_t num_query_tokens,
                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -402,6 +402,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   }
   if (int64_t(num_query_tokens) * num_heads * head_dim > (int64_t(1) << 40)) return PA_ERR_UNSUPPORTED;
   a.out = out;
+  a.lse = lse;
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -420,6 +421,70 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.scale = scale;
   a.scale_log2e = scale * 1.4426950408889634f;
   return status_of(pa::launch_prefill(a, head_dim, block_size, bf16, static_cast<hipStream_t>(stream)));
+}
+
+int pa_cp_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables,
+                       const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t block_size,
+                       int32_t cp_world, int32_t cp_rank, int32_t interleave, void* stream) {
+  if (num_tokens < 0 || num_seqs < 0 || max_blocks_per_seq < 0 || block_size < 1)
+    return PA_ERR_INVALID_ARG;
+  if (cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world || interleave < 1 ||
+      block_size % interleave != 0 || int64_t(block_size) * cp_world > 0x7FFFFFFF)
+    return PA_ERR_INVALID_ARG;
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping || !seq_ids || !positions) return PA_ERR_INVALID_ARG;
+  if (!block_tables && int64_t(num_seqs) * max_blocks_per_seq > 0) return PA_ERR_INVALID_ARG;
+  return status_of(pa::launch_cp_slot_mapping(slot_mapping, block_tables, seq_ids, positions,
+                                              num_tokens, num_seqs, max_blocks_per_seq, block_size,
+                                              cp_world, cp_rank, interleave,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int pa_cp_context_lens(int32_t* local_lens, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t block_size, int32_t cp_world, int32_t cp_rank, int32_t interleave,
+                       void* stream) {
+  if (num_seqs < 0 || block_size < 1 || cp_world < 1 || cp_rank < 0 || cp_rank >= cp_world ||
+      interleave < 1 || block_size % interleave != 0 || int64_t(block_size) * cp_world > 0x7FFFFFFF)
+    return PA_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PA_OK;
+  if (!local_lens || !context_lens) return PA_ERR_INVALID_ARG;
+  return status_of(pa::launch_cp_context_lens(local_lens, context_lens, num_seqs, block_size,
+                                              cp_world, cp_rank, interleave,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int pa_merge_states(void* out, float* out_lse, const void* states, const float* state_lses,
+                    int32_t num_states, int32_t num_rows, int32_t head_dim, int32_t dtype,
+                    void* stream) {
+  if (num_states < 1 || num_rows < 0 || head_dim < 4 || head_dim % 4 != 0)
+    return PA_ERR_INVALID_ARG;
+  if (elem_bytes_of(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (num_rows == 0) return PA_OK;
+  if (!out || !states || !state_lses) return PA_ERR_INVALID_ARG;
+  const uintptr_t align = dtype == PA_DTYPE_BF16 ? 8 : 16;
+  if ((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(states)) % align != 0)
+    return PA_ERR_INVALID_ARG;
+  if (int64_t(num_rows) * (head_dim / 4) / 256 >= 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  return status_of(pa::launch_merge_states(out, out_lse, states, state_lses, num_states, num_rows,
+                                           head_dim, dtype == PA_DTYPE_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int pa_map_to_kernel_blocks(int32_t* kernel_tables, const int32_t* manager_tables,
+                            int32_t num_rows, int32_t max_blocks_per_row,
+                            int32_t kernel_blocks_per_block, void* stream) {
+  if (num_rows < 0 || max_blocks_per_row < 0 || kernel_blocks_per_block < 1)
+    return PA_ERR_INVALID_ARG;
+  const int64_t n = int64_t(num_rows) * max_blocks_per_row * kernel_blocks_per_block;
+  if (n == 0) return PA_OK;
+  if (!kernel_tables || !manager_tables) return PA_ERR_INVALID_ARG;
+  if (int64_t(max_blocks_per_row) * kernel_blocks_per_block > 0x7FFFFFFF ||
+      (n + 255) / 256 > 0x7FFFFFFF)
+    return PA_ERR_UNSUPPORTED;
+  return status_of(pa::launch_map_to_kernel_blocks(kernel_tables, manager_tables, num_rows,
+                                                   max_blocks_per_row, kernel_blocks_per_block,
+                                                   static_cast<hipStream_t>(stream)));
 }
 
 int pa_append_decode_partials(void* out, const void* q, const void* key, const void* value,

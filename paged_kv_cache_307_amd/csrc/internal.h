@@ -41,6 +41,7 @@ struct DecodeArgs {
 // Arguments of one prefill launch.
 struct PrefillArgs {
   void* out;
+  float* lse;                  // [num_query_tokens][num_heads] log-sum-exp per row, or null
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -116,6 +117,19 @@ hipError_t launch_decode_simt(const DecodeArgs& a, int head_dim, int block_size,
                               hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_size, bool bf16,
                           hipStream_t stream);
+hipError_t launch_cp_slot_mapping(int64_t* slots, const int32_t* block_tables,
+                                  const int32_t* seq_ids, const int32_t* positions,
+                                  int num_tokens, int num_seqs, int max_blocks_per_seq,
+                                  int block_size, int world, int rank, int interleave,
+                                  hipStream_t stream);
+hipError_t launch_cp_context_lens(int32_t* local_lens, const int32_t* context_lens, int num_seqs,
+                                  int block_size, int world, int rank, int interleave,
+                                  hipStream_t stream);
+hipError_t launch_merge_states(void* out, float* out_lse, const void* states, const float* lses,
+                               int num_states, int64_t num_rows, int head_dim, bool bf16,
+                               hipStream_t stream);
+hipError_t launch_map_to_kernel_blocks(int32_t* kernel_tables, const int32_t* manager_tables,
+                                       int num_rows, int max_blocks, int k, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
                                hipStream_t stream);
 

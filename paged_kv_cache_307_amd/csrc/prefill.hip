@@ -322,6 +322,11 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const float l_tot = col_sum(l_run[c]);
+    if (col_ok[c] && a.lse && grp == 0) {
+      // ln sum_t e^(scale q.k_t) = (m + log2 l) ln 2, m and l in the log2 domain
+      a.lse[int64_t(q0 + qi[c]) * a.num_heads + qh[c]] =
+          l_tot > 0.f ? (m_run[c] + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
+    }
     if (col_ok[c]) {
       const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row that sees no token: zeros
       uint16_t* o = static_cast<uint16_t*>(a.out) +
@@ -381,6 +386,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
   }
   float* o = static_cast<float*>(a.out) + (int64_t(sr.q0 + i) * a.num_heads + h) * D;
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
+  if (a.lse && lane == 0)
+    a.lse[int64_t(sr.q0 + i) * a.num_heads + h] = l > 0.f ? m + logf(l) : -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) o[lane + 64 * e] = acc[e] * inv_l;
 }

@@ -181,7 +181,7 @@ def prefill_call(lib, **kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, S=4, T=64, Hq=32, Hkv=8,
              D=128, B=16, NB=100, MB=64, maxlen=1024, maxq=16, scale=0.088, dtype=BF16)
     a.update(kw)
-    return lib.pa_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"],
+    return lib.pa_prefill(a["out"], None, a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["S"],
                           a["T"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["MB"],
                           a["maxlen"], a["maxq"], a["scale"], a["dtype"], None)
 
@@ -206,3 +206,28 @@ def prefill_call(lib, **kw):
 ])
 def test_prefill_rejects_before_launch(lib, kw, expect):
     assert prefill_call(lib, **kw) == expect
+
+
+def test_context_parallel_calls_reject_before_launch(lib):
+    cs = lib.pa_cp_slot_mapping
+    assert cs(FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 16, 2, 1, 1, None) == OK
+    assert cs(FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 16, 2, 2, 1, None) == INVALID   # rank >= world
+    assert cs(FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 16, 0, 0, 1, None) == INVALID   # no ranks
+    assert cs(FAKE, FAKE, FAKE, FAKE, 0, 2, 8, 16, 2, 0, 3, None) == INVALID   # 3 does not divide 16
+    assert cs(None, FAKE, FAKE, FAKE, 5, 2, 8, 16, 2, 0, 1, None) == INVALID
+    cl = lib.pa_cp_context_lens
+    assert cl(FAKE, FAKE, 0, 16, 4, 3, 4, None) == OK
+    assert cl(FAKE, FAKE, 3, 16, 4, -1, 4, None) == INVALID
+    assert cl(None, FAKE, 3, 16, 4, 0, 4, None) == INVALID
+    ms = lib.pa_merge_states
+    assert ms(FAKE, None, FAKE, FAKE, 0, 10, 128, BF16, None) == INVALID       # no states
+    assert ms(FAKE, None, FAKE, FAKE, 2, 10, 126, BF16, None) == INVALID       # not 4-aligned dims
+    assert ms(FAKE, None, FAKE, FAKE, 2, 10, 128, 9, None) == UNSUPPORTED
+    assert ms(FAKE, None, FAKE, FAKE, 2, 0, 128, BF16, None) == OK
+    assert ms(FAKE, None, None, FAKE, 2, 10, 128, BF16, None) == INVALID
+    assert ms(FAKE_MISALIGNED - 4, None, FAKE, FAKE, 2, 10, 128, F32, None) == INVALID
+    mk = lib.pa_map_to_kernel_blocks
+    assert mk(FAKE, FAKE, 4, 8, 0, None) == INVALID
+    assert mk(FAKE, FAKE, 0, 8, 2, None) == OK
+    assert mk(None, FAKE, 4, 8, 2, None) == INVALID
+    assert mk(FAKE, FAKE, 4, 1 << 30, 4, None) == UNSUPPORTED
