@@ -57,8 +57,18 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False): {
-        "bytes": 553895046, "fetch_bytes": 549028902, "write_bytes": 4866144,
-        "sources_sha256": "609c5e8a8dae5a6c33642f6db3ab593f8fd19b04c216e59ef11142b2b5ae5dcf"},
+        "bytes": 553915501, "fetch_bytes": 549049360, "write_bytes": 4866140,
+        "sources_sha256": "7877eb80359da94f7c284f1f6d6c4966567dd5697b57123c8a11eecd541c8432"},
+}
+# The same two passes over `bench.py --workload llama3_8b_prefill` for
+# pa_prefill (summary: profiles/prefill_llama3_8b_prefill_hbm_bytes.md).
+PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_307_amd/csrc/device_common.h",
+                   "paged_kv_cache_307_amd/csrc/internal.h", "paged_kv_cache_307_amd/csrc/api.hip",
+                   "paged_kv_cache_307_amd/build.py"]
+PREFILL_TRAFFIC = {
+    "llama3_8b_prefill": {
+        "bytes": 297235396, "fetch_bytes": 230126532, "write_bytes": 67108864,
+        "sources_sha256": "656a6fc259d52aea0da0c103221be9f88ad4089451b5b72e3ef750ba0908aab2"},
 }
 
 
@@ -91,9 +101,9 @@ def algorithmic_bytes(w):
             "write": int((L > 0).sum()) * w.num_kv_heads * w.head_dim * e * 2}
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(sources=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -193,6 +203,15 @@ def host_block_manager_timing(w, steps=200):
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_WORKLOADS = {"llama3_8b_prefill"}
+
+
+def prefill_traffic(workload):
+    """Counter-derived HBM bytes per pa_prefill launch, or None when there is
+    no measurement or the kernel changed since."""
+    rec = PREFILL_TRAFFIC.get(workload)
+    if rec is None or rec["sources_sha256"] != kernel_sources_sha256(PREFILL_SOURCES):
+        return None
+    return rec["bytes"]
 
 
 def prefill_flops(w):
@@ -317,7 +336,7 @@ def run_prefill_bench(args):
             "kernel": "prefill_bf16_mfma_kernel<128,16,4,2> (pa_prefill)", "bound": "mfma",
             "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_us": round(attend_ms * 1e3, 3),
-            "flops_per_launch": F, "traffic": None,
+            "flops_per_launch": F, "traffic": prefill_traffic(w.name),
         },
         "cpu_baseline": cpu,
     }

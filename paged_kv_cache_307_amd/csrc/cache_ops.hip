@@ -71,6 +71,8 @@ __device__ __forceinline__ void store_row(Elem* __restrict__ k_cache, Elem* __re
 
 // Rows per workgroup of the write.
 constexpr int kWriteChunk = 256;
+// Below this many chunks the write also splits KV heads over workgroups.
+constexpr int kSplitHeadsBelowChunks = 512;
 // Largest (block, KV head) V tile the write transposes through LDS.
 constexpr int kTileLdsBytes = 32768;
 
@@ -255,8 +257,14 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const 
   const int tile_path = v_aligned && (int64_t(block_size) * elem_bytes % 16 == 0) &&
                         int64_t(block_size) * head_dim * elem_bytes <= kTileLdsBytes &&
                         block_size <= kWriteChunk;
-  const dim3 grid{unsigned(ceil_div(num_tokens, kWriteChunk)),
-                  unsigned(num_kv_heads < 65535 ? num_kv_heads : 65535)};
+  // Few chunks (a prefill chunk, a decode step): split each chunk's heads
+  // over workgroups so the write has enough of them; 8192 rows of 8 heads
+  // took 240 us as 32 workgroups and 71 us as 256.  Many chunks (a whole
+  // history) fill the device already, and one pass over all heads of a chunk
+  // measured faster there (131,759 rows: 337 us against 381 us split).
+  const int chunks = ceil_div(num_tokens, kWriteChunk);
+  const int split = chunks >= kSplitHeadsBelowChunks ? 1 : (num_kv_heads < 65535 ? num_kv_heads : 65535);
+  const dim3 grid{unsigned(chunks), unsigned(split)};
   if (elem_bytes == 4) {
     return launch(write_kv_kernel<uint32_t>, grid, dim3(kThreads), 0, stream,
                   static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
