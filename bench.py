@@ -67,8 +67,8 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
                    "paged_kv_cache_307_amd/build.py"]
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
-        "bytes": 297235396, "fetch_bytes": 230126532, "write_bytes": 67108864,
-        "sources_sha256": "656a6fc259d52aea0da0c103221be9f88ad4089451b5b72e3ef750ba0908aab2"},
+        "bytes": 297139159, "fetch_bytes": 230030295, "write_bytes": 67108864,
+        "sources_sha256": "e2a72ffdc900fb1c65f7c960c578b50620af931f44916d3abf357bd23c9c707f"},
 }
 
 
@@ -333,7 +333,7 @@ def run_prefill_bench(args):
         "query_tokens_per_s": round(w.num_query_tokens / (ms_per_step * 1e-3), 1),
         "flops_per_step": F,
         "roofline": {
-            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2> (pa_prefill)", "bound": "mfma",
+            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 2 waves per workgroup (pa_prefill)", "bound": "mfma",
             "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_us": round(attend_ms * 1e3, 3),
             "flops_per_launch": F, "traffic": prefill_traffic(w.name),

@@ -13,21 +13,22 @@
 // same table as decode; only the number of query rows differs.
 //
 // bf16 kernel.  For one (sequence, KV head) the query rows are the pairs
-// (position i, head of the group) in order, i * G + head; a wave takes 16 of
-// them as the 16 columns of the matrix-core tiles
+// (position i, head of the group) in order, i * G + head; a wave takes NC
+// tiles of 16 of them (64 rows at NC = 4) as the columns of the matrix-core
+// tiles
 //
 //   S^T[16 tok x 16 col] = K_tile[16 tok x D] . Q^T[D x 16 col]   (16x16x32 bf16)
 //   O^T[D x 16 col]     += V^T_tile[D x 16 tok] . P^T[16 tok x 16 col] (16x16x16 bf16)
 //
 // with the operand layouts of the decode kernel (lane l: row/column l & 15,
 // group l >> 4; K rows are 16-byte loads from the [B][D] tile, V columns
-// 8-byte loads from the token-innermost [D][B] tile).  Column c sees tokens
-// below its own limit lim_c = L - n + i_c + 1; tiles below the smallest
-// limit of the wave need no mask.  Four waves (64 consecutive rows) form a
-// workgroup and stream the same tiles, so three of the four reads of a tile
-// hit in the cache; the launch order keeps all row groups of one (sequence,
-// KV head) on one XCD (workgroup i runs on XCD i % 8), heaviest (latest
-// positions) first.
+// 8-byte loads from the token-innermost [D][B] tile), so each K/V tile feeds
+// NC products of each kind.  Column c sees tokens below its own limit
+// lim_c = L - n + i_c + 1; tiles below the smallest limit of the wave need
+// no mask.  The waves of a workgroup take consecutive rows and stream the
+// same tiles; the launch order keeps all row groups of one (sequence, KV
+// head) on one XCD (workgroup i runs on XCD i % 8), latest positions first,
+// so the re-reads of a tile by later row groups hit that XCD's L2.
 //
 // fp32 kernel.  One wave per (query row, head): lanes hold D / 64 dims each;
 // each token's dot product is reduced across the wave.  It exists for the
@@ -47,10 +48,13 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 2;  // waves per workgroup (4 measured 1.5% slower, 1 3%)
 constexpr int kTile = 16;
 constexpr float kRescale = 8.0f;  // lazy maximum: weights stay <= 2^8
 constexpr int kXcds = 8;
+// Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data
+// format, no swizzle (the loads are untyped 16- and 8-byte fetches).
+constexpr int kRawWord3 = 0x00020000;
 
 __device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
   float2_t f = {lo, hi};
@@ -119,16 +123,23 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
   pb0 = bad0 ? 0 : pb0;
   pb1 = bad1 ? 0 : pb1;
   if constexpr (B >= kTile) {
+    // The tile's K and V bases are wave-uniform (one block): scalar buffer
+    // descriptors, and each lane adds the same 32-bit offset to every tile,
+    // instead of a 64-bit address per lane and load.
     const int in_block = t0 % B;
-    const char* kb = kc + (int64_t(pb0) * a.num_kv_heads + kvh) * kTileBytes +
-                     (int64_t(in_block) * D + int64_t(col) * D) * 2 + grp * 16;
-    const char* vb = vc + (int64_t(pb0) * a.num_kv_heads + kvh) * kTileBytes +
-                     (in_block + int64_t(col) * B) * 2 + grp * 8;
+    const int64_t tile = (int64_t(pb0) * a.num_kv_heads + kvh) * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kc + tile + int64_t(in_block) * D * 2), 0, int(kTileBytes), kRawWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(vc + tile + in_block * 2), 0, int(kTileBytes), kRawWord3);
+    const int k_off = col * D * 2 + grp * 16;
+    const int v_off = col * B * 2 + grp * 8;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) r.k[j] = *reinterpret_cast<const uint4*>(kb + 64 * j);
+    for (int j = 0; j < D / 32; ++j)
+      r.k[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * j, 0));
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-      r.v[c] = *reinterpret_cast<const uint2*>(vb + int64_t(32) * B * c);
+      r.v[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 32 * B * c, 0));
     r.bad = bad0;
   } else {
     const bool k_second = col >= B;
@@ -394,9 +405,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
 
 // Column tiles per wave of the bf16 kernel for head_dim D (the larger D, the
 // more registers a column tile holds).  Measured on the 16-sequence,
-// 512-token-chunk layer at D = 128: 1 tile per wave 2.02 ms, 2 tiles 1.14 ms,
-// 4 tiles 0.98 ms; two or three register tiles in the ring made no
-// difference.
+// 512-token-chunk layer at D = 128 (accumulators in VGPRs, see build.py):
+// 1 tile per wave ~2.0 ms, 2 tiles 1.04-1.08 ms (also at two waves per SIMD),
+// 4 tiles 0.82-0.85 ms; a third register tile in the ring changed nothing.
 template <int D>
 constexpr int prefill_nc() { return D >= 256 ? 2 : 4; }
 constexpr int kPrefillRing = 2;
