@@ -260,7 +260,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
           r.v[d].y &= my;
         }
       }
-      const bool edge = t0 + kTile > lim_min;
+      // wave-uniform: a scalar branch skips the masks on interior tiles
+      const bool edge = __builtin_amdgcn_readfirstlane(int(t0 + kTile > lim_min)) != 0;
+      const bool bad = __builtin_amdgcn_readfirstlane(int(r.bad)) != 0;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] = tb + i < lim[c] ? x[i] : -INFINITY;
         }
-        if (r.bad) {
+        if (bad) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
         }
