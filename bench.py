@@ -343,6 +343,108 @@ def run_prefill_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def run_cp_bench(args):
+    """Context-parallel decode of the 64-sequence layer over W ranks emulated
+    on one GPU (one pool per rank): each rank's pa_decode_lse over the tokens
+    it owns, then pa_merge_states.  Prints one JSON line; value = one rank's
+    decode GB/s (a rank runs on its own GPU in a real deployment)."""
+    import workloads as W_
+
+    import torch
+
+    import paged_kv_cache_307_amd as pa
+    pa.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    world, inter = args.cp_world, 1
+    w = W_.llama3_8b_decode()
+    B = w.block_size
+
+    def t(x):
+        x = np.ascontiguousarray(x)
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    # one table for every rank: virtual blocks of B * world tokens, shuffled ids
+    nvb = [-(-int(L) // (B * world)) for L in w.context_lens]
+    ids = np.random.default_rng(307_390).permutation(sum(nvb))
+    table = np.full((w.num_seqs, max(nvb)), -1, dtype=np.int32)
+    k = 0
+    for s_, n in enumerate(nvb):
+        table[s_, :n] = ids[k:k + n]
+        k += n
+    seq = np.concatenate([w.hist_seq, w.new_seq])
+    pos = np.concatenate([w.hist_pos, w.new_pos])
+    key = t(np.concatenate([w.hist_key, w.new_key]))
+    val = t(np.concatenate([w.hist_value, w.new_value]))
+    bt, cl, q = t(table), t(w.context_lens), t(w.q)
+    ranks = []
+    for r in range(world):
+        kc, vc = pa.empty_kv_cache(len(ids), w.num_kv_heads, B, w.head_dim, torch.bfloat16, dev,
+                                   fill=float("nan"))
+        pa.write_kv(kc, vc, key, val, pa.cp_slot_mapping(bt, t(seq), t(pos), B, world, r, inter))
+        local = pa.cp_context_lens(cl, B, world, r, inter)
+        mcl = int(local.max().item())
+        ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl,
+                                4096, dev)
+        # the rank's pool in args.layers copies, rotated per step like the
+        # decode bench, so K/V come from HBM rather than the last-level cache
+        pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(args.layers - 1)]
+        ranks.append((pools, local, mcl, ws))
+    outs = torch.empty((world,) + tuple(q.shape), dtype=q.dtype, device=dev)
+    lses = torch.empty((world, w.num_seqs, w.num_heads), dtype=torch.float32, device=dev)
+    merged = torch.empty_like(q)
+
+    def rank_decode(r, i):
+        pools, local, mcl, ws = ranks[r]
+        kc, vc = pools[i % len(pools)]
+        pa.decode(q, kc, vc, bt, local, mcl, w.scale, partition_size=4096, workspace=ws,
+                  out=outs[r], lse=lses[r])
+
+    def step(i):
+        for r in range(world):
+            rank_decode(r, i)
+        pa.merge_states(outs, lses, out=merged)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    for i in range(args.steps):
+        rank_decode(0, i)
+    ev[1].record()
+    for _ in range(args.steps):
+        pa.merge_states(outs, lses, out=merged)
+    ev[2].record()
+    torch.cuda.synchronize()
+    rank_ms = ev[0].elapsed_time(ev[1]) / args.steps
+    merge_ms = ev[1].elapsed_time(ev[2]) / args.steps
+    local0 = ranks[0][1].cpu().numpy().astype(np.int64)
+    e = 2
+    rank_bytes = int(local0.sum()) * w.num_kv_heads * w.head_dim * 2 * e + 2 * q.numel() * e
+    gbs = rank_bytes / (rank_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "context-parallel paged decode: one rank's HBM GB/s", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(rank_ms + merge_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama3_8b_decode over {world} context-parallel ranks",
+                   "batch": w.num_seqs, "cp_world": world, "interleave": inter,
+                   "layers_rotated": args.layers,
+                   "rank0_tokens": int(local0.sum()),
+                   "step": "per rank pa_decode_lse (partials + merge); pa_merge_states"},
+        "rank_decode_us": round(rank_ms * 1e3, 3), "merge_states_us": round(merge_ms * 1e3, 3),
+        "roofline": {"kernel": "pa_decode_lse of rank 0 (decode + merge launches)", "bound": "hbm",
+                     "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_us": round(rank_ms * 1e3, 3),
+                     "bytes_per_launch": rank_bytes, "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +459,8 @@ def main():
                     help="write the step's rows with pa_write_kv, then pa_decode_partials")
     ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
                     help="PA_DECODE_SHARED_BLOCKS: auto = when the tables share blocks")
+    ap.add_argument("--cp-world", type=int, default=0,
+                    help="context-parallel ranks to emulate on the decode layer (0 = off)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks on a known byte count (profiler calibration)")
     args = ap.parse_args()
@@ -368,6 +472,9 @@ def main():
         return
     if args.workload in PREFILL_WORKLOADS:
         run_prefill_bench(args)
+        return
+    if args.cp_world > 0:
+        run_cp_bench(args)
         return
 
     w, default_partition = make_workload(args.workload)

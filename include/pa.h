@@ -333,6 +333,21 @@ int pa_prefill(void* out, float* lse, const void* q, const void* k_cache, const 
                int32_t max_query_len, float scale, int32_t dtype, void* stream);
 
 /*
+ * pa_decode_lse -- pa_decode that also writes, for every (sequence, query
+ * head), the natural log of sum_t exp(scale * q . K_t) over its context:
+ *   lse  out  fp32 [num_seqs][num_heads] (-inf for a sequence of length 0)
+ * Other arguments, results and errors as pa_decode; PA_ERR_INVALID_ARG for a
+ * NULL lse when num_seqs > 0.  This is what pa_merge_states needs to combine
+ * decodes over disjoint token sets, e.g. the context-parallel ranks below.
+ */
+int pa_decode_lse(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                  int32_t dtype, int32_t flags, void* stream);
+
+/*
  * Context parallelism.
  * [P2 BlockTable walkthrough: under decode / prefill context parallelism the
  *  slot mapping uses a virtual block size and a mask, and writes -1 for the
@@ -346,8 +361,8 @@ int pa_prefill(void* out, float* lse, const void* q, const void* k_cache, const 
  * ranks 0 .. cp_world-1 in turn, and a rank packs the runs it owns into the
  * block_size slots of its copy of the block, in order.  A rank's tokens thus
  * form an ordinary paged sequence in its own pool, whose length
- * pa_cp_context_lens gives: any decode or prefill call attends over it, and
- * pa_merge_states combines the ranks' results (each with its log-sum-exp).
+ * pa_cp_context_lens gives: pa_decode_lse (or pa_prefill with lse) attends
+ * over it, and pa_merge_states combines the ranks' results.
  * cp_world = 1 is the plain mapping.  Exchanging the partial results between
  * GPUs is the caller's (one all-gather of out and lse per step).
  */

@@ -25,7 +25,7 @@ EXPORTED = (
     "pa_status_string", "pa_slot_mapping", "pa_write_kv", "pa_copy_blocks",
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partials", "pa_decode_merge",
     "pa_append_decode", "pa_append_decode_partials", "pa_prefill", "pa_cp_slot_mapping",
-    "pa_cp_context_lens", "pa_merge_states", "pa_map_to_kernel_blocks",
+    "pa_cp_context_lens", "pa_merge_states", "pa_map_to_kernel_blocks", "pa_decode_lse",
 )
 
 
@@ -67,6 +67,8 @@ def load_library():
     }
     sig["pa_prefill"] = (ctypes.c_int,
                          [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P])
+    sig["pa_decode_lse"] = (ctypes.c_int,
+                            [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, I, P])
     sig["pa_cp_slot_mapping"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, I, I, I, P])
     sig["pa_cp_context_lens"] = (ctypes.c_int, [P, P, I, I, I, I, I, P])
     sig["pa_merge_states"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, P])
@@ -228,10 +230,13 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_conte
 
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-           partition_size=0, workspace=None, out=None, stream=None, shared_blocks=False):
+           partition_size=0, workspace=None, out=None, stream=None, shared_blocks=False,
+           lse=None):
     """out[s, h] = softmax(scale q.K^T) V over the paged context of sequence s.
     shared_blocks: some blocks are read by more than one sequence (a cache
-    hint, PA_DECODE_SHARED_BLOCKS; results are the same either way)."""
+    hint, PA_DECODE_SHARED_BLOCKS; results are the same either way).
+    lse: an fp32 [S, Hq] tensor that receives each row's log-sum-exp
+    (pa_decode_lse)."""
     if out is None:
         out = torch.empty_like(q)
     dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
@@ -239,6 +244,15 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, sca
     if partition_size and workspace is None:
         workspace = alloc_workspace(s, hq, hkv, d, mcl, partition_size, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if lse is not None:
+        _cuda_contig("lse", lse, torch.float32)
+        _need(tuple(lse.shape) == (s, hq), "lse must be [S, Hq]")
+        st = load_library().pa_decode_lse(
+            _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+            _ptr(context_lens), s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size),
+            _ptr(workspace), ws_bytes, _dtype_code(q), _flags(shared_blocks), _stream(stream))
+        _check(st, "pa_decode_lse")
+        return out
     st = load_library().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _ptr(workspace),

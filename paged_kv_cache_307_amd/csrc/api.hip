@@ -487,6 +487,27 @@ int pa_map_to_kernel_blocks(int32_t* kernel_tables, const int32_t* manager_table
                                                    static_cast<hipStream_t>(stream)));
 }
 
+int pa_decode_lse(void* out, float* lse, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                  int32_t dtype, int32_t flags, void* stream) {
+  DecodePlan plan;
+  const int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                             workspace_bytes, dtype, flags);
+  if (st != PA_OK || plan.args.num_seqs == 0) return st;
+  if (!lse) return PA_ERR_INVALID_ARG;
+  plan.args.lse = lse;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_partials(plan, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (plan.split) e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);
+  return status_of(e);
+}
+
 int pa_append_decode_partials(void* out, const void* q, const void* key, const void* value,
                               void* k_cache, void* v_cache, const int32_t* block_tables,
                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

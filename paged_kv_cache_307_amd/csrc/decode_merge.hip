@@ -154,6 +154,7 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
   PairRecords pr;
   if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
     for (int i = lane + wave * kThreads; i < D; i += kThreads * NW) out[i] = from_f32<Elem>(0.f);
+    if (a.lse && threadIdx.x == 0) a.lse[int64_t(s) * a.num_heads + h] = -INFINITY;
     return;
   }
   if (pr.whole) return;  // written whole by its worker
@@ -202,6 +203,8 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
     for (int w = 1; w < NW; ++w)
       if (lane < CH) fold_into(f, part[w][lane]);
   }
+  if (a.lse && lane == 0)  // ln sum e^(scale q.k) = (m + log2 den) ln 2
+    a.lse[int64_t(s) * a.num_heads + h] = (f.m + __log2f(f.den)) * 0.6931471805599453f;
   if (lane < CH) {
     const float inv = 1.0f / f.den;
 #pragma unroll

@@ -522,6 +522,9 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     auto finish = [&]() {
       if (whole) {
         const float l_tot = colsum4(l_run);
+        if (a.lse && col < G && grp == 0)  // ln sum e^(scale q.k) = (m + log2 l) ln 2
+          a.lse[int64_t(s) * a.num_heads + int64_t(kvh) * G + col] =
+              (m_run + __log2f(l_tot)) * 0.6931471805599453f;
         if (col < G) {
           const float inv_l = 1.0f / l_tot;
           uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G + col) * D + 4 * grp;
@@ -663,6 +666,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     if (L == 0) {
       uint16_t* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G) * D;
       for (int i = lane; i < G * D; i += kThreads) o[i] = 0;
+      if (a.lse && lane < G) a.lse[int64_t(s) * a.num_heads + int64_t(kvh) * G + lane] = -INFINITY;
       return;
     }
     run(s, kvh, L, 0, (L + kTile - 1) / kTile, true, PairSlots{0, 0}, 0);

@@ -161,6 +161,9 @@ __global__ __launch_bounds__(64) void decode_simt_kernel(DecodeArgs a, int B) {
       if (h >= G) continue;
       const float l_tot = wave_sum(l_part[h]);
       if (whole) {
+        if (a.lse && lane == 0)  // ln sum e^(scale q.k) = (m + log2 l) ln 2
+          a.lse[int64_t(s) * a.num_heads + int64_t(kvh) * G + h] =
+              (m_run[h] + __log2f(l_tot)) * 0.6931471805599453f;
         Elem* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G + h) * D;
 #pragma unroll
         for (int k = 0; k < DPL; ++k) o[lane + 64 * k] = from_f32<Elem>(acc[h][k] / l_tot);
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(64) void decode_simt_kernel(DecodeArgs a, int B) {
     if (L == 0) {
       Elem* o = out + (int64_t(s) * a.num_heads + int64_t(kvh) * G) * D;
       for (int i = lane; i < G * D; i += 64) o[i] = from_f32<Elem>(0.f);
+      if (a.lse && lane < G) a.lse[int64_t(s) * a.num_heads + int64_t(kvh) * G + lane] = -INFINITY;
       return;
     }
     piece(s, kvh, L, 0, (L + 15) / 16, true, 0);

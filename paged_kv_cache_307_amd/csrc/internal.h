@@ -20,6 +20,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   const void* new_k;          // append: K row [S][Hkv][D] of each sequence's token L - 1, or null
   const void* new_v;          // append: V row, same shape
+  float* lse;                 // [S][Hq] log-sum-exp of each (sequence, head), or null
   float* ws;                  // split-KV records (see schedule.h), nullptr in single pass
   void* ws_meta;              // split-KV meta block: prefT, prefP, N
   int32_t workers;            // split-KV worker grid

@@ -40,6 +40,7 @@ def _virtual_table(w, world):
     return table, max(1, len(ids))
 
 
+@pytest.mark.parametrize("rank_call", ["decode_lse", "prefill"])
 @pytest.mark.parametrize("dt,world,inter,B,Hq,Hkv,D", [
     ("f32", 2, 1, 16, 4, 2, 64),
     ("bf16", 2, 1, 16, 32, 8, 128),
@@ -48,8 +49,8 @@ def _virtual_table(w, world):
     ("f32", 4, 16, 16, 4, 4, 128),
     ("bf16", 8, 2, 32, 16, 4, 128),
 ])
-def test_context_parallel_decode(dt, world, inter, B, Hq, Hkv, D):
-    _say(f"cp decode {dt} W={world} I={inter} B={B} Hq={Hq} Hkv={Hkv} D={D}")
+def test_context_parallel_decode(dt, world, inter, B, Hq, Hkv, D, rank_call):
+    _say(f"cp decode {dt} W={world} I={inter} B={B} Hq={Hq} Hkv={Hkv} D={D} via {rank_call}")
     lens = [1, 2, 17, 40, 100, 257, 600, B * world, B * world + 1]
     w = W.custom(lens, Hq, Hkv, D, B, dt, seed=307_350 + world * 10 + inter)
     ref = oracle.run_step(w)["out"]
@@ -78,7 +79,12 @@ def test_context_parallel_decode(dt, world, inter, B, Hq, Hkv, D):
         oracle.write_kv(kp, vp, key, val, ref_slots, B)
         assert np.array_equal(bits(k), kp) and np.array_equal(bits(v), vp), f"rank {r} pools"
         lse = torch.empty((w.num_seqs, Hq), dtype=torch.float32, device="cuda")
-        out = pa.prefill(q, k, v, bt, local, starts, max(max(ref_local), 1), 1, w.scale, lse=lse)
+        if rank_call == "prefill":
+            out = pa.prefill(q, k, v, bt, local, starts, max(max(ref_local), 1), 1, w.scale,
+                             lse=lse)
+        else:
+            out = pa.decode(q, k, v, bt, local, max(max(ref_local), 1), w.scale,
+                            partition_size=2 * B * (r % 2), lse=lse)
         outs.append(out)
         lses.append(lse)
     merged = pa.merge_states(torch.stack(outs), torch.stack(lses))
@@ -86,6 +92,37 @@ def test_context_parallel_decode(dt, world, inter, B, Hq, Hkv, D):
     err = float(np.max(np.abs(as_f64(merged) - ref)))
     _say(f"  merged vs unsplit decode: max abs err {err:.3e}")
     assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("dt,P", [("bf16", 0), ("bf16", 32), ("bf16", 512), ("f32", 0),
+                                  ("f32", 64)])
+def test_decode_lse_matches_oracle(dt, P):
+    """pa_decode_lse: outputs as pa_decode and each row's log-sum-exp, single
+    pass and split (whole pairs from the decode kernel, split pairs from the
+    merge), with empty sequences giving -inf."""
+    lens = [1, 0, 17, 40, 100, 700, 1500, 33, 0, 4000]
+    w = W.custom([max(L, 1) for L in lens], 32, 8, 128, 16, dt, seed=307_380 + P)
+    r = oracle.run_step(w)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    k, v = pa.empty_kv_cache(w.num_blocks, 8, 16, 128, tdt, "cuda", fill=float("nan"))
+    kb, vb = r["k_pool"], r["v_pool"]
+    k.copy_(dev(kb if dt == "bf16" else kb.view(np.float32)))
+    v.copy_(dev(vb if dt == "bf16" else vb.view(np.float32)))
+    cl = np.array(lens, dtype=np.int32)
+    lse = torch.empty((w.num_seqs, 32), dtype=torch.float32, device="cuda")
+    out = pa.decode(_rows(w.q, dt), k, v, dev(w.block_tables), dev(cl), w.max_context_len,
+                    w.scale, partition_size=P, lse=lse)
+    torch.cuda.synchronize()
+    starts = np.arange(w.num_seqs + 1, dtype=np.int32)
+    ref_out, ref_lse = oracle.prefill_lse(oracle.to_bits(w.q, dt), kb, vb, w.block_tables, cl,
+                                          starts, w.scale, 8, 16, dt)
+    assert float(np.max(np.abs(as_f64(out) - ref_out))) <= TOL[dt]
+    got = lse.cpu().numpy().astype(np.float64)
+    empty = cl == 0
+    assert np.isneginf(got[empty]).all()
+    tol = 1e-5 if dt == "f32" else 2e-2
+    assert float(np.max(np.abs(got[~empty] - ref_lse[~empty]) /
+                        np.maximum(1.0, np.abs(ref_lse[~empty])))) <= tol
 
 
 def test_prefill_lse_matches_oracle():
