@@ -263,45 +263,71 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
       // wave-uniform: a scalar branch skips the masks on interior tiles
       const bool edge = __builtin_amdgcn_readfirstlane(int(t0 + kTile > lim_min)) != 0;
       const bool bad = __builtin_amdgcn_readfirstlane(int(r.bad)) != 0;
+      // The NC column tiles are independent; each phase runs over all of them
+      // so that their products and softmax chains interleave in one basic
+      // block (a branch per column tile would fence each chain off).
+      floatx4_t sacc[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) sacc[c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
+                                                            qop[c][j], sacc[c], 0, 0, 0);
+      }
+      float x[NC][4];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[c][i] = sacc[c][i] * a.scale_log2e;
+      if (edge) {  // causal edge (and the tail): per-column limit
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[c][i] = tb + i < lim[c] ? x[c][i] : -INFINITY;
+      }
+      if (bad) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[c][i] = __builtin_nanf("");
+      }
+      float tmax[NC];
+      bool grow = false;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        tmax[c] = col_max(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])));
+        grow |= tmax[c] > m_run[c] + kRescale;
+      }
+      if (__any(grow)) {  // rare: one branch for all column tiles
 #pragma unroll
-        for (int j = 0; j < KSTEPS; ++j)
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
-                                                         qop[c][j], sacc, 0, 0, 0);
-        float x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
-        if (edge) {  // causal edge (and the tail): per-column limit
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = tb + i < lim[c] ? x[i] : -INFINITY;
-        }
-        if (bad) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
-        }
-        const float tmax = col_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-        if (__any(tmax > m_run[c] + kRescale)) {
-          const float m_new = fmaxf(m_run[c], tmax);
+        for (int c = 0; c < NC; ++c) {
+          const float m_new = fmaxf(m_run[c], tmax[c]);
           const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
           l_run[c] *= alpha;
 #pragma unroll
           for (int d = 0; d < DCH; ++d) acc[c][d] *= alpha;
           m_run[c] = m_new;
         }
+      }
+      short4_t pop[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
         const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];  // sees nothing yet
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[c][i] - m_use);
         l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        const uint2 pp = make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3]));
-        const short4_t pop = __builtin_bit_cast(short4_t, pp);
-#pragma unroll
-        for (int d = 0; d < DCH; ++d)
-          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(short4_t, r.v[d]), pop, acc[c][d], 0, 0, 0);
+        pop[c] = __builtin_bit_cast(short4_t,
+                                    make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3])));
       }
+#pragma unroll
+      for (int d = 0; d < DCH; ++d)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(short4_t, r.v[d]), pop[c], acc[c][d], 0, 0, 0);
     };
 
     // Ring of RING register tiles; every load is issued unconditionally (the
