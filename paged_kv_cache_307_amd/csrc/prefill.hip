@@ -52,6 +52,7 @@ constexpr int kWaves = 2;  // waves per workgroup (4 measured 1.5% slower, 1 3%)
 constexpr int kTile = 16;
 constexpr float kRescale = 8.0f;  // lazy maximum: weights stay <= 2^8
 constexpr int kXcds = 8;
+constexpr uint32_t kNanPair = 0x7FC07FC0u;  // two bfloat16 quiet NaNs
 // Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data
 // format, no swizzle (the loads are untyped 16- and 8-byte fetches).
 constexpr int kRawWord3 = 0x00020000;
@@ -105,12 +106,12 @@ template <int D>
 struct KVTile {
   uint4 k[D / 32];
   uint2 v[D / 16];
-  bool bad;
 };
 
 // Loads of the 16-token tile at t0 of KV head kvh (ids of its block(s) in
 // pb0 / pb1; pb1 is the second block of a B = 8 tile).  Out-of-range ids
-// read block 0 and mark the tile bad.
+// read block 0, and the K rows of their tokens become NaN, so every logit
+// of those tokens and every output that sees them is NaN.
 template <int D, int B>
 __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a, int pb0, int pb1,
                                              int kvh, int t0, int lane) {
@@ -140,7 +141,12 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       r.v[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 32 * B * c, 0));
-    r.bad = bad0;
+    // A bad block id poisons the tile's K with NaN, so the products carry
+    // it into every logit of the tile (rare; the branch is wave-uniform).
+    if (__builtin_amdgcn_readfirstlane(int(bad0))) {
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) r.k[j] = make_uint4(kNanPair, kNanPair, kNanPair, kNanPair);
+    }
   } else {
     const bool k_second = col >= B;
     const bool v_second = grp >= 2;
@@ -155,7 +161,13 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
       r.v[c] = *reinterpret_cast<const uint2*>(vb + int64_t(32) * B * c);
-    r.bad = v_second ? bad1 : bad0;
+    // K row `col` comes from the block of token `col`; a bad id there
+    // poisons that token's logits in every column
+    if (k_second ? bad1 : bad0) {
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) r.k[j] = make_uint4(kNanPair, kNanPair, kNanPair, kNanPair);
+    }
+    (void)v_second;
   }
 }
 
@@ -230,6 +242,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
   }
 
   if (t_end > 0) {
+    // c = |scale| log2 e; for a negative scale the sign goes into q (exact:
+    // a sign-bit flip of each bf16 element)
+    const float cpos = fabsf(a.scale_log2e);
+    const uint32_t qsign = a.scale_log2e < 0.f ? 0x80008000u : 0u;
     bf16x8_t qop[NC][KSTEPS];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -239,6 +255,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
       for (int j = 0; j < KSTEPS; ++j) {
         uint4 v = make_uint4(0, 0, 0, 0);
         if (col_ok[c]) v = *reinterpret_cast<const uint4*>(qp + 32 * j);
+        v.x ^= qsign;
+        v.y ^= qsign;
+        v.z ^= qsign;
+        v.w ^= qsign;
         qop[c][j] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
@@ -262,7 +282,6 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
       }
       // wave-uniform: a scalar branch skips the masks on interior tiles
       const bool edge = __builtin_amdgcn_readfirstlane(int(t0 + kTile > lim_min)) != 0;
-      const bool bad = __builtin_amdgcn_readfirstlane(int(r.bad)) != 0;
       // The NC column tiles are independent; each phase runs over all of them
       // so that their products and softmax chains interleave in one basic
       // block (a branch per column tile would fence each chain off).
@@ -276,28 +295,25 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
           sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
                                                             qop[c][j], sacc[c], 0, 0, 0);
       }
+      // raw q.k (q's sign carries the sign of the scale, so the scale
+      // factor c = |scale| log2 e is positive and max(c x) = c max(x)); the
+      // factor is applied inside the exponent's fused multiply-add
       float x[NC][4];
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[c][i] = sacc[c][i] * a.scale_log2e;
+        for (int i = 0; i < 4; ++i) x[c][i] = sacc[c][i];
       if (edge) {  // causal edge (and the tail): per-column limit
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[c][i] = tb + i < lim[c] ? x[c][i] : -INFINITY;
       }
-      if (bad) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[c][i] = __builtin_nanf("");
-      }
       float tmax[NC];
       bool grow = false;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        tmax[c] = col_max(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3])));
+        tmax[c] = col_max(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]))) * cpos;
         grow |= tmax[c] > m_run[c] + kRescale;
       }
       if (__any(grow)) {  // rare: one branch for all column tiles
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
         const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];  // sees nothing yet
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[c][i] - m_use);
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[c][i], cpos, -m_use));
         l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         pop[c] = __builtin_bit_cast(short4_t,
                                     make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3])));

@@ -103,6 +103,23 @@ def test_prefill_bad_block_id_gives_nan_not_fault():
     assert float(np.max(np.abs(out[8:] - ref[8:]))) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,bad_block", [(8, 1), (8, 3), (16, 1), (32, 0)])
+def test_prefill_bad_block_poisons_exactly_the_rows_that_see_it(B, bad_block):
+    """A whole 40-token prompt whose logical block `bad_block` has an id
+    outside the pool: rows at positions before that block are exact, rows
+    that see it are NaN (B = 8 puts two blocks in one 16-token tile, either
+    half of which may be the bad one)."""
+    w = W.prefill([40, 40], [40, 40], 8, 2, 128, B, "bf16", seed=307_334 + B)
+    table = w.block_tables.copy()
+    table[0, bad_block] = w.num_blocks + 3
+    out = as_f64(run_prefill_gpu(w, table=table))
+    ref = oracle.run_prefill(w)["out"]
+    first_bad = bad_block * B
+    assert float(np.max(np.abs(out[:first_bad] - ref[:first_bad]), initial=0.0)) <= TOL["bf16"]
+    assert np.isnan(out[first_bad:40]).all()
+    assert float(np.max(np.abs(out[40:] - ref[40:]))) <= TOL["bf16"]
+
+
 def test_prefill_rows_clamped_to_max_query_len():
     """Rows beyond max_query_len are not written; the others are exact."""
     w = W.prefill([30, 30], [10, 10], 8, 2, 64, 16, "bf16", seed=307_333)
