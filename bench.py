@@ -67,8 +67,8 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
                    "paged_kv_cache_307_amd/build.py"]
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
-        "bytes": 297141199, "fetch_bytes": 230032335, "write_bytes": 67108864,
-        "sources_sha256": "379ac71fb72310802c87854f23c1e0ebf893abd4fc2c7dea5c08ad85fee552e2"},
+        "bytes": 297144259, "fetch_bytes": 230035395, "write_bytes": 67108864,
+        "sources_sha256": "ae6de9bb7dde933ffacaf4379b3864132cf7e34e0de251114104d7a5427b827e"},
 }
 
 

@@ -120,6 +120,18 @@ def test_prefill_bad_block_poisons_exactly_the_rows_that_see_it(B, bad_block):
     assert float(np.max(np.abs(out[40:] - ref[40:]))) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_negative_and_large_scales(dt):
+    """The scale is any finite factor: a negative one (the bf16 kernel moves
+    its sign into q) and a large one (peaked softmax) against the oracle."""
+    for scale in (-0.09, 0.9):
+        w = W.prefill([5, 40, 130], [5, 7, 64], 8, 2, 64, 16, dt, seed=307_335)
+        w = W.PrefillWorkload(**{**w.__dict__, "scale": scale})
+        out = as_f64(run_prefill_gpu(w))
+        ref = oracle.run_prefill(w)["out"]
+        assert float(np.max(np.abs(out - ref))) <= TOL[dt], scale
+
+
 def test_prefill_rows_clamped_to_max_query_len():
     """Rows beyond max_query_len are not written; the others are exact."""
     w = W.prefill([30, 30], [10, 10], 8, 2, 64, 16, "bf16", seed=307_333)
