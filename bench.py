@@ -360,6 +360,9 @@ def run_cp_bench(args):
     world, inter = args.cp_world, 1
     w = W_.llama3_8b_decode()
     B = w.block_size
+    # the oracle computes the same result unsplit; its rate per KV byte does
+    # not depend on which tokens a rank holds
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
 
     def t(x):
         x = np.ascontiguousarray(x)
@@ -441,7 +444,7 @@ def run_cp_bench(args):
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_us": round(rank_ms * 1e3, 3),
                      "bytes_per_launch": rank_bytes, "traffic": None},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
 
