@@ -97,8 +97,11 @@ def algorithmic_bytes(w):
     kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * e
     q = w.num_seqs * w.num_heads * w.head_dim * e
     table = int(sum(-(-int(x) // w.block_size) for x in L)) * 4
+    # copy-on-write before the step (the shared-prefix fork step): each pair
+    # reads and writes one whole block of K and of V
+    copy = len(w.copy_pairs) * 2 * 2 * w.num_kv_heads * w.block_size * w.head_dim * e
     return {"kv": kv, "q": q, "out": q, "table": table, "context_lens": 4 * w.num_seqs,
-            "write": int((L > 0).sum()) * w.num_kv_heads * w.head_dim * e * 2}
+            "write": int((L > 0).sum()) * w.num_kv_heads * w.head_dim * e * 2, "copy": copy}
 
 
 def kernel_sources_sha256(sources=None):
@@ -515,6 +518,10 @@ def main():
     new_k, new_v, q = t(w.new_key), t(w.new_value), t(w.q)
     out = torch.empty_like(q)
     mcl = w.max_context_len
+    # the fork step copies each shared partial block into its branch's
+    # private block first; repeating the copy every step restores the same
+    # state (the sources never change, and each branch then rewrites its slot)
+    copies = t(w.copy_pairs) if len(w.copy_pairs) else None
     ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, P, dev)
     torch.cuda.synchronize()
 
@@ -527,8 +534,10 @@ def main():
                                       shared_blocks=shared)
 
     def step(i):
+        k, v = layers[i % len(layers)]
+        if copies is not None:
+            pa.copy_blocks(k, v, copies)
         if args.separate_write:
-            k, v = layers[i % len(layers)]
             pa.write_kv(k, v, new_k, new_v, new_slots)
         partials(i)
         pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
@@ -558,6 +567,16 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     part_avg_ms = ev0.elapsed_time(ev1) / args.steps
+    copy_us = None
+    if copies is not None:  # the copy launch alone, the same way
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            k, v = layers[i % len(layers)]
+            pa.copy_blocks(k, v, copies)
+        ev1.record()
+        torch.cuda.synchronize()
+        copy_us = round(ev0.elapsed_time(ev1) / args.steps * 1e3, 3)
 
     ms_per_step = elapsed * 1e3 / args.steps
     ab = algorithmic_bytes(w)
@@ -590,12 +609,15 @@ def main():
             "context_len_mean": round(float(L.mean()), 1), "num_blocks": w.num_blocks,
             "partition_size": P, "layers_rotated": args.layers,
             "kv_loads": "cached (PA_DECODE_SHARED_BLOCKS)" if shared else "streamed (nontemporal)",
-            "step": ("pa_write_kv + pa_decode_partials + pa_decode_merge" if args.separate_write
-                     else "pa_append_decode_partials + pa_decode_merge"),
+            "step": (("pa_copy_blocks + " if copies is not None else "") +
+                     ("pa_write_kv + pa_decode_partials + pa_decode_merge" if args.separate_write
+                      else "pa_append_decode_partials + pa_decode_merge")),
+            "copy_pairs": len(w.copy_pairs),
         },
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
+        "copy_blocks_us": copy_us,
         "roofline": {
             "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true,{str(not shared).lower()},"
                       f"{str(multi_part).lower()}> (" +
