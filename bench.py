@@ -143,6 +143,7 @@ def cpu_baseline(w, budget_s=12.0):
         q = oracle.to_bits(w.q, w.dtype)
         reps, t0 = 0, time.perf_counter()
         while True:
+            oracle.copy_blocks(k_pool, v_pool, w.copy_pairs)  # the fork step's copies (if any)
             ns = oracle.slot_mapping(w.block_tables, w.new_seq, w.new_pos, B)
             oracle.write_kv(k_pool, v_pool, oracle.to_bits(w.new_key, w.dtype),
                             oracle.to_bits(w.new_value, w.dtype), ns, B)
@@ -157,8 +158,29 @@ def cpu_baseline(w, budget_s=12.0):
     step_bytes = sum(ab.values())
     return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "tokens_per_s": round(w.num_seqs / step_s, 2),
-            "sample": f"{reps} full steps (write + decode, all {w.num_seqs} sequences) of the "
-                      f"same workload, single thread, {el:.1f} s"}
+            "sample": f"{reps} full steps (copies if any, write + decode, all {w.num_seqs} "
+                      f"sequences) of the same workload, single thread, {el:.1f} s",
+            "block_manager_us_per_step": model_block_manager_timing(w)}
+
+
+def model_block_manager_timing(w, steps=50):
+    """The CPU model of the block manager on the same pattern as
+    host_block_manager_timing: us per 64-sequence append plus table export."""
+    from oracle import block_manager as bm
+
+    B, S = w.block_size, w.num_seqs
+    grow = -(-steps // B) + 1
+    mb = w.max_blocks_per_seq + grow
+    nb = int(sum(-(-max(int(L) - 1, 0) // B) for L in w.context_lens)) + S * grow
+    mgr = bm.BlockManager(nb, B, S, mb, np.random.default_rng(0).permutation(nb))
+    for s_ in range(S):
+        assert mgr.allocate(s_, int(w.context_lens[s_]) - 1)[0] == 0
+    seqs = list(range(S))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        assert mgr.append(seqs)[0] == 0
+        mgr.block_tables(seqs)
+    return round((time.perf_counter() - t0) * 1e6 / steps, 2)
 
 
 def copy_calibration(pairs=2048, reps=5):
