@@ -494,7 +494,7 @@ def main():
                     help="only run pa_copy_blocks on a known byte count (profiler calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: measures one GPU only (the path is single-GPU); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
