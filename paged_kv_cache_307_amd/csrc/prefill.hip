@@ -25,7 +25,8 @@
 // 8-byte loads from the token-innermost [D][B] tile), so each K/V tile feeds
 // NC products of each kind.  Column c sees tokens below its own limit
 // lim_c = L - n + i_c + 1; tiles below the smallest limit of the wave need
-// no mask.  The waves of a workgroup take consecutive rows and stream the
+// no mask.  Block ids are scalar loads fetched one tile ahead of the tile
+// loads.  The waves of a workgroup take consecutive rows and stream the
 // same tiles; the launch order keeps all row groups of one (sequence, KV
 // head) on one XCD (workgroup i runs on XCD i % 8), latest positions first,
 // so the re-reads of a tile by later row groups hit that XCD's L2.
@@ -169,22 +170,6 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
     }
     (void)v_second;
   }
-}
-
-// Block-table window: lane i holds the id of logical block wb + i (clamped to
-// the sequence's last block), so one vector load serves 64 blocks and a
-// tile's id comes from a lane read instead of a scalar load whose latency
-// would sit in front of every tile's loads.
-__device__ __forceinline__ int table_window(const int32_t* trow, int wb, int nblk, int lane) {
-  return trow[min(wb + lane, nblk - 1)];
-}
-
-template <int B>
-__device__ __forceinline__ void tile_ids(int win, int wb, int k, int nblk, int& pb0, int& pb1) {
-  const int lb = k * kTile / B;
-  pb0 = __builtin_amdgcn_readlane(win, lb - wb);
-  pb1 = pb0;
-  if constexpr (B < kTile) pb1 = lb + 1 < nblk ? __builtin_amdgcn_readlane(win, lb + 1 - wb) : pb0;
 }
 
 // NC: 16-row column tiles per wave (each K/V tile feeds NC products of each
@@ -348,20 +333,25 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 
     // Ring of RING register tiles; every load is issued unconditionally (the
     // index clamped to the last tile) so each wait covers exactly the loads
-    // before it.  Block ids come from a table window reloaded when a tile's
-    // blocks leave it.
+    // before it.
     KVTile<D> ring[RING];
-    int wb = 0;
-    int win = table_window(trow, 0, nblk, lane);
+    // Block ids are scalar loads fetched one issue ahead: a tile's vector
+    // loads then wait only for its own ids (the scalar counter), never for
+    // the tiles still in flight (a vector-register table window would make
+    // every issue wait for all outstanding vector loads).
+    auto fetch_ids = [&](int k, int& p0, int& p1) {
+      k = wave_uniform(min(k, last));  // a scalar index: a scalar load
+      const int lb = k * kTile / B;
+      p0 = load_ro(trow, lb);
+      p1 = p0;
+      if constexpr (B < kTile) p1 = lb + 1 < nblk ? load_ro(trow, lb + 1) : p0;
+    };
+    int next0, next1;
+    fetch_ids(0, next0, next1);
     auto issue = [&](KVTile<D>& r, int k) {
-      k = min(k, last);
-      if (k * kTile / B - wb + (B < kTile ? 1 : 0) >= 64) {  // wave-uniform
-        wb = k * kTile / B;
-        win = table_window(trow, wb, nblk, lane);
-      }
-      int pb0, pb1;
-      tile_ids<B>(win, wb, k, nblk, pb0, pb1);
-      load_kv_tile<D, B>(r, a, pb0, pb1, kvh, k * kTile, lane);
+      const int pb0 = wave_uniform(next0), pb1 = wave_uniform(next1);
+      load_kv_tile<D, B>(r, a, pb0, pb1, kvh, min(k, last) * kTile, lane);
+      fetch_ids(k + 1, next0, next1);
     };
 #pragma unroll
     for (int d = 0; d < RING - 1; ++d) issue(ring[d], d);
@@ -451,10 +441,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
 // more registers a column tile holds).  Measured on the 16-sequence,
 // 512-token-chunk layer at D = 128 (accumulators in VGPRs, see build.py):
 // 1 tile per wave ~2.0 ms, 2 tiles 1.04-1.08 ms (also at two waves per SIMD),
-// 4 tiles 0.82-0.85 ms; a third register tile in the ring changed nothing.
+// 4 tiles 0.82-0.85 ms.  Three register tiles in the load ring: 742 -> 716
+// us once block ids became scalar loads (with ids from a vector register
+// every issue waited for all loads in flight, and the depth did not matter).
 template <int D>
 constexpr int prefill_nc() { return D >= 256 ? 2 : 4; }
-constexpr int kPrefillRing = 2;
+constexpr int kPrefillRing = 3;
 
 template <int D>
 hipError_t launch_bf16_d(PrefillArgs a, int block_size, hipStream_t stream) {
