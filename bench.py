@@ -67,8 +67,8 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
                    "paged_kv_cache_307_amd/build.py"]
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
-        "bytes": 297144259, "fetch_bytes": 230035395, "write_bytes": 67108864,
-        "sources_sha256": "ae6de9bb7dde933ffacaf4379b3864132cf7e34e0de251114104d7a5427b827e"},
+        "bytes": 297214882, "fetch_bytes": 230106018, "write_bytes": 67108864,
+        "sources_sha256": "6f01bba23170da303983db48d8c09701b6174b906544265bee910c032fee04df"},
 }
 
 
@@ -359,7 +359,7 @@ def run_prefill_bench(args):
         "query_tokens_per_s": round(w.num_query_tokens / (ms_per_step * 1e-3), 1),
         "flops_per_step": F,
         "roofline": {
-            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 2 waves per workgroup (pa_prefill)", "bound": "mfma",
+            "kernel": "prefill_bf16_mfma_kernel<128,16,4,3>, 2 waves per workgroup (pa_prefill)", "bound": "mfma",
             "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_us": round(attend_ms * 1e3, 3),
             "flops_per_launch": F, "traffic": prefill_traffic(w.name),
