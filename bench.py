@@ -67,8 +67,8 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
                    "paged_kv_cache_307_amd/build.py"]
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
-        "bytes": 297214882, "fetch_bytes": 230106018, "write_bytes": 67108864,
-        "sources_sha256": "6f01bba23170da303983db48d8c09701b6174b906544265bee910c032fee04df"},
+        "bytes": 297214245, "fetch_bytes": 230105381, "write_bytes": 67108864,
+        "sources_sha256": "0be249d1d31d4919db74a05176a56f1a6359f76eaf7f53b9bec5085bc382fbc3"},
 }
 
 
