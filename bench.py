@@ -104,6 +104,21 @@ def algorithmic_bytes(w):
             "write": int((L > 0).sum()) * w.num_kv_heads * w.head_dim * e * 2, "copy": copy}
 
 
+def capacity_figures(w):
+    """What paging costs and saves on this batch (the pages' capacity
+    arithmetic): unused tail slots of the last blocks, the fragmentation
+    proxy 1 - used / allocated slots, and the slots a max-length contiguous
+    reservation (the table's capacity) would leave unused."""
+    B = w.block_size
+    L = w.context_lens.astype(np.int64)
+    alloc = int(sum(-(-int(x) // B) * B for x in L))
+    used = int(L.sum())
+    max_len = w.max_blocks_per_seq * B
+    return {"tail_waste_slots": alloc - used,
+            "fragmentation_proxy": round(1.0 - used / alloc, 6) if alloc else 0.0,
+            "max_len": max_len, "prealloc_waste_slots": int(w.num_seqs * max_len - used)}
+
+
 def kernel_sources_sha256(sources=None):
     h = hashlib.sha256()
     for rel in (KERNEL_SOURCES if sources is None else sources):
@@ -640,6 +655,7 @@ def main():
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
         "copy_blocks_us": copy_us,
+        "capacity": capacity_figures(w),
         "roofline": {
             "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true,{str(not shared).lower()},"
                       f"{str(multi_part).lower()}> (" +
