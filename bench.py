@@ -604,6 +604,19 @@ def main():
     ev1.record()
     torch.cuda.synchronize()
     part_avg_ms = ev0.elapsed_time(ev1) / args.steps
+    # Per-launch distribution of the same kernel: an event pair around each
+    # launch (each pair adds its own small gap, so these read a few percent
+    # above the back-to-back average).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        partials(i)
+        e1.record()
+    torch.cuda.synchronize()
+    per_launch_us = np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])
+    launch_pct = {f"p{q}": round(float(np.percentile(per_launch_us, q)), 3) for q in (10, 50, 90)}
     copy_us = None
     if copies is not None:  # the copy launch alone, the same way
         torch.cuda.synchronize()
@@ -662,7 +675,8 @@ def main():
                       ("pa_decode_partials" if args.separate_write else "pa_append_decode_partials") + ")",
             "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
-            "avg_us": round(part_avg_ms * 1e3, 3), "bytes_per_launch": part_bytes,
+            "avg_us": round(part_avg_ms * 1e3, 3), "per_launch_us": launch_pct,
+            "bytes_per_launch": part_bytes,
             "traffic": measured_traffic(w.name, P, not args.separate_write, shared),
         },
         "cpu_baseline": cpu,
