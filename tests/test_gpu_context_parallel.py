@@ -197,3 +197,54 @@ def test_kernel_tables_from_allocator_tables(k, Bk):
     assert np.array_equal(bits(kc), kp) and np.array_equal(bits(vc), vp)
     ref = oracle.decode(wm.q, kp, vp, ref_kt, wm.context_lens, wm.scale, 2, Bk, "bf16")
     assert float(np.max(np.abs(as_f64(out) - ref))) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("world", [2, 4, 8])
+def test_full_llama3_8b_context_parallel(world):
+    """The 64-sequence Llama-3-8B-shaped layer over W ranks, in the launch
+    configuration the context-parallel benchmark times: one shared table of
+    virtual blocks (B * W tokens, shuffled ids), interleave 1, one pool per
+    rank, pa_decode_lse with 4096-token partitions and a workspace, then
+    pa_merge_states.  Rank slots and local lengths bit for bit, the merged
+    output against the oracle's unsplit decode of every row."""
+    w = W.llama3_8b_decode()
+    B, inter = w.block_size, 1
+    _say(f"full cp decode W={world}: {w.num_seqs} seqs, lengths {int(w.context_lens.min())}.."
+         f"{int(w.context_lens.max())}")
+    ref = oracle.run_step(w)["out"]
+    nvb = [-(-int(L) // (B * world)) for L in w.context_lens]
+    ids = np.random.default_rng(307_390).permutation(sum(nvb)).astype(np.int32)
+    table = np.full((w.num_seqs, max(nvb)), -1, dtype=np.int32)
+    k0 = 0
+    for s, n in enumerate(nvb):
+        table[s, :n] = ids[k0:k0 + n]
+        k0 += n
+    seq = np.concatenate([w.hist_seq, w.new_seq])
+    pos = np.concatenate([w.hist_pos, w.new_pos])
+    key = np.concatenate([w.hist_key, w.new_key])
+    val = np.concatenate([w.hist_value, w.new_value])
+    bt, sq, ps, cl = dev(table), dev(seq), dev(pos), dev(w.context_lens)
+    key_d, val_d, q = dev(key), dev(val), dev(w.q)
+    outs = torch.empty((world,) + tuple(q.shape), dtype=q.dtype, device="cuda")
+    lses = torch.empty((world, w.num_seqs, w.num_heads), dtype=torch.float32, device="cuda")
+    for r in range(world):
+        k, v = pa.empty_kv_cache(len(ids), w.num_kv_heads, B, w.head_dim, torch.bfloat16, "cuda",
+                                 fill=float("nan"))
+        slots = pa.cp_slot_mapping(bt, sq, ps, B, world, r, inter)
+        assert np.array_equal(slots.cpu().numpy(),
+                              oracle.cp_slot_mapping(table, seq, pos, B, world, r, inter)), r
+        pa.write_kv(k, v, key_d, val_d, slots)
+        local = pa.cp_context_lens(cl, B, world, r, inter)
+        ref_local = [oracle.cp_context_len(int(L), B, world, r, inter) for L in w.context_lens]
+        assert local.cpu().tolist() == ref_local, r
+        mcl = max(ref_local)
+        ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, 4096,
+                                "cuda")
+        pa.decode(q, k, v, bt, local, mcl, w.scale, partition_size=4096, workspace=ws,
+                  out=outs[r], lse=lses[r])
+        del k, v
+    merged = pa.merge_states(outs, lses)
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(as_f64(merged) - ref)))
+    _say(f"  merged vs unsplit decode: max abs err {err:.3e}")
+    assert err <= TOL["bf16"]
