@@ -392,11 +392,10 @@ int pa_prefill(void* out, float* lse, const void* q, const void* k_cache, const 
   const bool bf16 = dtype == PA_DTYPE_BF16;
   pa::PrefillArgs a{};
   if (bf16) {
-    const int64_t row_groups = (int64_t(max_query_len) * group + 63) / 64;
-    const int64_t work = row_groups * num_kv_heads * num_seqs;
-    if (work > 0x7FFFFFF8) return PA_ERR_UNSUPPORTED;
-    a.row_groups = int32_t(row_groups);
-    a.work = int32_t(work);
+    // the launch's workgroups at the smallest row group (32 rows, D = 256),
+    // the pairs rounded up to the 8 XCDs
+    const int64_t row_groups = (int64_t(max_query_len) * group + 31) / 32;
+    if ((int64_t(num_kv_heads) * num_seqs + 7) * row_groups > 0x7FFFFFF8) return PA_ERR_UNSUPPORTED;
   } else if (num_heads > 65535 || num_seqs > 65535) {
     return PA_ERR_UNSUPPORTED;
   }

@@ -58,8 +58,7 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;     // clamp for context_lens
   int32_t max_query_len;       // clamp for query rows per sequence
-  int32_t row_groups;          // bf16: ceil(max_query_len * group / 64)
-  int32_t work;                // bf16: num_seqs * num_kv_heads * row_groups
+  int32_t row_groups;          // bf16: ceil(max_query_len * group / rows of one workgroup)
   float scale;
   float scale_log2e;
 };

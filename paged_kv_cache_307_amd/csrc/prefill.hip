@@ -186,14 +186,19 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
   const int col = lane & 15;
   const int grp = lane >> 4;
 
-  // XCD-grouped work index: workgroups that run on one XCD take consecutive
-  // work items, i.e. the row groups of one (sequence, KV head).
-  const int per_xcd = gridDim.x / kXcds;
-  const int w = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (w >= a.work) return;
-  const int rg = a.row_groups - 1 - w % a.row_groups;  // latest positions first
-  const int kvh = (w / a.row_groups) % a.num_kv_heads;
-  const int s = w / (a.row_groups * a.num_kv_heads);
+  // XCD-aware work index.  Workgroup i runs on XCD i % 8 and is that XCD's
+  // j-th, j = i / 8.  The (sequence, KV head) pairs are dealt to the XCDs in
+  // turn (pair p to XCD p % 8), and an XCD takes the row groups of its pairs
+  // one pair after another: every row group of a pair reads the pair's tiles
+  // through one L2, and the XCDs' shares are alike whatever the sequences'
+  // lengths (with 8 KV heads, XCD x takes KV head x of every sequence).
+  const int xcd = blockIdx.x % kXcds;
+  const int j = blockIdx.x / kXcds;
+  const int pair = xcd + kXcds * (j / a.row_groups);
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int rg = a.row_groups - 1 - j % a.row_groups;  // latest positions first
+  const int kvh = pair % a.num_kv_heads;
+  const int s = pair / a.num_kv_heads;
   const SeqRows sr = seq_rows(a, s, B);
   const int L = wave_uniform(sr.L), n = wave_uniform(sr.n), q0 = wave_uniform(sr.q0);
   const int nrows = wave_uniform(sr.rows) * G;
@@ -452,7 +457,9 @@ template <int D>
 hipError_t launch_bf16_d(PrefillArgs a, int block_size, hipStream_t stream) {
   constexpr int NC = prefill_nc<D>();
   constexpr int RING = kPrefillRing;
-  const int64_t groups = (int64_t(a.work) + kXcds - 1) / kXcds * kXcds;
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
+  const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * a.row_groups;
+  if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
   const dim3 grid{unsigned(groups)}, block{unsigned(kWaves * 64)};
   switch (block_size) {
     case 8: return launch(prefill_bf16_mfma_kernel<D, 8, NC, RING>, grid, block, 0, stream, a);
@@ -479,7 +486,6 @@ hipError_t launch_prefill(const PrefillArgs& a0, int head_dim, int block_size, b
   if (bf16) {
     const int64_t rows = prefill_group_rows(head_dim);
     a.row_groups = int32_t((int64_t(a.max_query_len) * a.group + rows - 1) / rows);
-    a.work = a.row_groups * a.num_kv_heads * a.num_seqs;
     switch (head_dim) {
       case 64: return launch_bf16_d<64>(a, block_size, stream);
       case 128: return launch_bf16_d<128>(a, block_size, stream);

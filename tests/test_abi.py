@@ -199,6 +199,7 @@ def prefill_call(lib, **kw):
     (dict(out=FAKE_MISALIGNED), INVALID),
     (dict(scale=float("inf")), INVALID),
     (dict(S=1 << 20, Hq=64, Hkv=64, maxq=1 << 12), UNSUPPORTED),   # grid beyond 2^31 workgroups
+    (dict(S=1024, Hq=8, Hkv=8, D=256, maxq=10_000_000), UNSUPPORTED),  # 32-row groups at D = 256
     (dict(S=70000, dtype=F32), UNSUPPORTED),                         # fp32 grid's z limit
     (dict(S=0), OK),
     (dict(T=0), OK),
