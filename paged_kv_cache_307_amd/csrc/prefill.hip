@@ -192,10 +192,28 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
   // one pair after another: every row group of a pair reads the pair's tiles
   // through one L2, and the XCDs' shares are alike whatever the sequences'
   // lengths (with 8 KV heads, XCD x takes KV head x of every sequence).
+  // Longest first: when an XCD holds at most 64 pairs, its k-th pair is the
+  // one of rank k by context length (descending, ties by index), so the
+  // longest waves start first and short ones fill the end.  Every workgroup
+  // ranks the same lengths, so each pair is taken exactly once.
   const int xcd = blockIdx.x % kXcds;
   const int j = blockIdx.x / kXcds;
-  const int pair = xcd + kXcds * (j / a.row_groups);
-  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int pairs = a.num_seqs * a.num_kv_heads;
+  const int k = j / a.row_groups;                         // slot among the XCD's pairs
+  const int px = (pairs - xcd + kXcds - 1) / kXcds;       // pairs on this XCD
+  if (k >= px) return;
+  int pair = xcd + kXcds * k;
+  if (px <= 64) {
+    const int mine = xcd + kXcds * min(lane, px - 1);
+    const int key = load_ro(a.context_lens, mine / a.num_kv_heads);
+    int rank = 0;
+    for (int m = 0; m < px; ++m) {
+      const int km = __builtin_amdgcn_readlane(key, m);
+      rank += (km > key || (km == key && m < lane)) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(lane < px && rank == k);
+    if (hit) pair = xcd + kXcds * int(__builtin_ctzll(hit));
+  }
   const int rg = a.row_groups - 1 - j % a.row_groups;  // latest positions first
   const int kvh = pair % a.num_kv_heads;
   const int s = pair / a.num_kv_heads;
