@@ -63,13 +63,22 @@ __device__ __forceinline__ uint32_t pack2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
+// IEEE maximum (a NaN operand gives NaN).  It maps to one v_maximum3_f32,
+// where fmaxf (maxNum, which drops a NaN operand) first quiets each operand
+// that is not known to be canonical with an extra v_max_f32 -- every lane
+// swap result and matrix-core output here.  Only tile maxima use it: a
+// column that sees a NaN logit is NaN through its exponentials either way.
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // max / sum of x over the four row groups of an MFMA result column (lanes
 // l, l ^ 16, l ^ 32, l ^ 48), via gfx950 lane swaps.
 __device__ __forceinline__ float col_max(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  x = max_nan(__uint_as_float(s[0]), __uint_as_float(s[1]));
   s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return max_nan(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float col_sum(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
       bool grow = false;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        tmax[c] = col_max(fmaxf(fmaxf(x[c][0], x[c][1]), fmaxf(x[c][2], x[c][3]))) * cpos;
+        tmax[c] = col_max(max_nan(max_nan(x[c][0], x[c][1]), max_nan(x[c][2], x[c][3]))) * cpos;
         grow |= tmax[c] > m_run[c] + kRescale;
       }
       if (__any(grow)) {  // rare: one branch for all column tiles
