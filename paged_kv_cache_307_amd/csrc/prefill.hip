@@ -249,13 +249,17 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
   }
 
   floatx4_t acc[NC][DCH];
-  float m_run[NC], l_run[NC];
+  // m_run: the maximum in use; neg_m: -m_run, or 0 while the column has
+  // seen nothing (m_run = -inf), the exponent's offset, kept beside m_run
+  // since it changes only when m_run does
+  float m_run[NC], l_run[NC], neg_m[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
 #pragma unroll
     for (int d = 0; d < DCH; ++d) acc[c][d] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     m_run[c] = -INFINITY;
     l_run[c] = 0.f;
+    neg_m[c] = 0.f;
   }
 
   if (t_end > 0) {
@@ -342,15 +346,15 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 #pragma unroll
           for (int d = 0; d < DCH; ++d) acc[c][d] *= alpha;
           m_run[c] = m_new;
+          neg_m[c] = m_new == -INFINITY ? 0.f : -m_new;
         }
       }
       short4_t pop[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const float m_use = m_run[c] == -INFINITY ? 0.f : m_run[c];  // sees nothing yet
         float pr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[c][i], cpos, -m_use));
+        for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[c][i], cpos, neg_m[c]));
         l_run[c] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
         pop[c] = __builtin_bit_cast(short4_t,
                                     make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3])));
