@@ -48,11 +48,18 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 1;  // waves per workgroup (best of three, chunked layer: 1 -> 704 us, 2 -> 713, 4 -> 720)
 constexpr int kTile = 16;
 constexpr float kRescale = 8.0f;  // lazy maximum: weights stay <= 2^8
 constexpr int kXcds = 8;
+// The Q operands of a wave's column tiles (NC x D/32 16-byte pieces per
+// lane) wait in LDS, read just before each product, instead of in
+// registers: with them resident, accumulators + Q + load ring exceed the
+// 256 vector registers and the compiler parks Q in accumulation registers,
+// copying it back before every product.
+constexpr bool kQInLds = true;
 constexpr uint32_t kNanPair = 0x7FC07FC0u;  // two bfloat16 quiet NaNs
 // Word 3 of a raw buffer descriptor on gfx9-family parts: 32-bit data
 // format, no swizzle (the loads are untyped 16- and 8-byte fetches).
@@ -267,7 +274,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
     // a sign-bit flip of each bf16 element)
     const float cpos = fabsf(a.scale_log2e);
     const uint32_t qsign = a.scale_log2e < 0.f ? 0x80008000u : 0u;
-    bf16x8_t qop[NC][KSTEPS];
+    __shared__ __align__(16) u32x4_t q_lds[kQInLds ? kWaves * NC * KSTEPS * 64 : 1];
+    bf16x8_t qop[kQInLds ? 1 : NC][KSTEPS];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
@@ -280,13 +288,30 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
         v.y ^= qsign;
         v.z ^= qsign;
         v.w ^= qsign;
-        qop[c][j] = __builtin_bit_cast(bf16x8_t, v);
+        if constexpr (kQInLds)
+          q_lds[((wave * NC + c) * KSTEPS + j) * 64 + lane] = u32x4_t{v.x, v.y, v.z, v.w};
+        else
+          qop[c][j] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
     const int32_t* trow = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
     const int nblk = (L + B - 1) / B;
     const int ntile = (t_end + kTile - 1) / kTile;
     const int last = ntile - 1;
+
+    // Q^T operand of column tile c, step j.  The LDS read is volatile so that
+    // it stays in the loop, next to its product, instead of being hoisted
+    // out of it into registers.
+    auto q_operand = [&](int c, int j) -> bf16x8_t {
+      if constexpr (kQInLds) {
+        typedef __attribute__((address_space(3))) const volatile u32x4_t lds_q_t;
+        const lds_q_t* p =
+            (const lds_q_t*)(&q_lds[((wave * NC + c) * KSTEPS + j) * 64 + lane]);
+        return __builtin_bit_cast(bf16x8_t, u32x4_t(*p));
+      } else {
+        return qop[c][j];
+      }
+    };
 
     auto consume = [&](KVTile<D>& r, int k) {
       const int t0 = k * kTile;
@@ -314,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 #pragma unroll
         for (int c = 0; c < NC; ++c)
           sacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
-                                                            qop[c][j], sacc[c], 0, 0, 0);
+                                                            q_operand(c, j), sacc[c], 0, 0, 0);
       }
       // raw q.k (q's sign carries the sign of the scale, so the scale
       // factor c = |scale| log2 e is positive and max(c x) = c max(x)); the
@@ -477,12 +502,14 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
 // more registers a column tile holds).  Measured on the 16-sequence,
 // 512-token-chunk layer at D = 128 (accumulators in VGPRs, see build.py):
 // 1 tile per wave ~2.0 ms, 2 tiles 1.04-1.08 ms (also at two waves per SIMD),
-// 4 tiles 0.82-0.85 ms.  Three register tiles in the load ring: 742 -> 716
-// us once block ids became scalar loads (with ids from a vector register
-// every issue waited for all loads in flight, and the depth did not matter).
+// 4 tiles 0.82-0.85 ms.  Two register tiles in the load ring: with Q in LDS
+// the kernel then needs 246 vector registers and no accumulation registers,
+// so two waves share each SIMD (446 us on that layer, against 645 with a
+// third ring tile, 282 registers, one wave per SIMD, and 511 with Q in
+// registers and three ring tiles).
 template <int D>
 constexpr int prefill_nc() { return D >= 256 ? 2 : 4; }
-constexpr int kPrefillRing = 3;
+constexpr int kPrefillRing = 2;
 
 template <int D>
 hipError_t launch_bf16_d(PrefillArgs a, int block_size, hipStream_t stream) {
