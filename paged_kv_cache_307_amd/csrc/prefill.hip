@@ -256,10 +256,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
   }
 
   floatx4_t acc[NC][DCH];
-  // m_run: the maximum in use; neg_m: -m_run, or 0 while the column has
-  // seen nothing (m_run = -inf), the exponent's offset, kept beside m_run
-  // since it changes only when m_run does
-  float m_run[NC], l_run[NC], neg_m[NC];
+  // m_run: the maximum in use (of c q.k, c = |scale| log2 e, see cpos).  Kept beside
+  // it, since they change only when m_run does: neg_m = -m_run, or 0 while
+  // the column has seen nothing (m_run = -inf), the exponent's offset; and
+  // thr = (m_run + kRescale) / c, the raw q.k a tile's maximum must exceed
+  // for a rescale.
+  float m_run[NC], l_run[NC], neg_m[NC], thr[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -267,12 +269,18 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
     m_run[c] = -INFINITY;
     l_run[c] = 0.f;
     neg_m[c] = 0.f;
+    thr[c] = -INFINITY;
   }
 
   if (t_end > 0) {
     // c = |scale| log2 e; for a negative scale the sign goes into q (exact:
     // a sign-bit flip of each bf16 element)
-    const float cpos = fabsf(a.scale_log2e);
+    // Masked logits are -inf and meet c in the exponent's fused multiply-add,
+    // so c is kept at least FLT_MIN: a zero scale would give -inf * 0 = NaN.
+    // At |scale log2 e| < FLT_MIN every weight is then 2^(q.k FLT_MIN - m)
+    // instead of 2^(q.k scale log2 e - m), both 1 to fp32 precision.
+    const float cpos = fmaxf(fabsf(a.scale_log2e), 1.17549435e-38f);
+    const float inv_c = 1.0f / cpos;
     const uint32_t qsign = a.scale_log2e < 0.f ? 0x80008000u : 0u;
     __shared__ __align__(16) u32x4_t q_lds[kQInLds ? kWaves * NC * KSTEPS * 64 : 1];
     bf16x8_t qop[kQInLds ? 1 : NC][KSTEPS];
@@ -355,23 +363,24 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 #pragma unroll
           for (int i = 0; i < 4; ++i) x[c][i] = tb + i < lim[c] ? x[c][i] : -INFINITY;
       }
-      float tmax[NC];
+      float tmax[NC];  // raw q.k
       bool grow = false;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        tmax[c] = col_max(max_nan(max_nan(x[c][0], x[c][1]), max_nan(x[c][2], x[c][3]))) * cpos;
-        grow |= tmax[c] > m_run[c] + kRescale;
+        tmax[c] = col_max(max_nan(max_nan(x[c][0], x[c][1]), max_nan(x[c][2], x[c][3])));
+        grow |= tmax[c] > thr[c];
       }
       if (__any(grow)) {  // rare: one branch for all column tiles
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const float m_new = fmaxf(m_run[c], tmax[c]);
+          const float m_new = fmaxf(m_run[c], tmax[c] * cpos);
           const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
           l_run[c] *= alpha;
 #pragma unroll
           for (int d = 0; d < DCH; ++d) acc[c][d] *= alpha;
           m_run[c] = m_new;
           neg_m[c] = m_new == -INFINITY ? 0.f : -m_new;
+          thr[c] = (m_new + kRescale) * inv_c;
         }
       }
       short4_t pop[NC];
