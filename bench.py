@@ -67,8 +67,8 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
                    "paged_kv_cache_307_amd/build.py"]
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
-        "bytes": 297214245, "fetch_bytes": 230105381, "write_bytes": 67108864,
-        "sources_sha256": "0be249d1d31d4919db74a05176a56f1a6359f76eaf7f53b9bec5085bc382fbc3"},
+        "bytes": 297752750, "fetch_bytes": 230643886, "write_bytes": 67108864,
+        "sources_sha256": "e3a02c9d0010517eaf9e5f999a41826d9f119d647c8da9b0ef1567b7af65c240"},
 }
 
 
@@ -374,7 +374,7 @@ def run_prefill_bench(args):
         "query_tokens_per_s": round(w.num_query_tokens / (ms_per_step * 1e-3), 1),
         "flops_per_step": F,
         "roofline": {
-            "kernel": "prefill_bf16_mfma_kernel<128,16,4,3>, 1 wave per workgroup (pa_prefill)", "bound": "mfma",
+            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 1 wave per workgroup, Q in LDS (pa_prefill)", "bound": "mfma",
             "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_us": round(attend_ms * 1e3, 3),
             "flops_per_launch": F, "traffic": prefill_traffic(w.name),
