@@ -194,13 +194,21 @@ __device__ __forceinline__ void load_tile(Tile<D>& r, const DecodeArgs& a, const
   }
 }
 
+// IEEE maximum (a NaN operand gives NaN): one v_maximum3_f32, where fmaxf
+// first quiets every operand not known to be canonical (lane swap results,
+// matrix-core outputs) with an extra v_max_f32.  Only tile maxima use it; a
+// column with a NaN logit is NaN through its exponentials either way.
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // x and its values in lanes l ^ 16, l ^ 32, l ^ 48 (the four row groups of
 // an MFMA result column), combined with max or +, via gfx950 lane swaps.
 __device__ __forceinline__ float colmax4(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  x = max_nan(__uint_as_float(s[0]), __uint_as_float(s[1]));
   s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return max_nan(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ float colsum4(float x) {
   auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -568,7 +576,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
       }
-      const float tmax = colmax4(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+      const float tmax = colmax4(max_nan(max_nan(x[0], x[1]), max_nan(x[2], x[3])));
       if (__any(tmax > m_run + kRescaleThreshold)) {
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
