@@ -57,8 +57,8 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False): {
-        "bytes": 553917355, "fetch_bytes": 549051211, "write_bytes": 4866144,
-        "sources_sha256": "b4215949fa76cd0576691acbd44a6fadd6f77aff259001dcb8bd8937dcdba3e4"},
+        "bytes": 553867967, "fetch_bytes": 549001823, "write_bytes": 4866144,
+        "sources_sha256": "6f946f039748493493f0909c691cea37e47ddb3517aa81b8a2104a1b97bee7fe"},
 }
 # The same two passes over `bench.py --workload llama3_8b_prefill` for
 # pa_prefill (summary: profiles/prefill_llama3_8b_prefill_hbm_bytes.md).
