@@ -49,7 +49,7 @@ SHAPES = [  # Hq, Hkv, D, B, dtype
     (4, 2, 64, 16, "f32"), (12, 4, 64, 32, "f32"), (8, 2, 256, 8, "f32"),
     (8, 2, 128, 16, "bf16"), (8, 8, 64, 8, "bf16"), (32, 8, 128, 16, "bf16"),
     (16, 1, 128, 32, "bf16"), (6, 2, 256, 8, "bf16"), (64, 8, 128, 16, "bf16"),
-    (4, 4, 256, 32, "bf16"),
+    (4, 4, 256, 32, "bf16"), (10, 2, 64, 32, "bf16"), (12, 2, 256, 16, "bf16"),
 ]
 
 
@@ -77,6 +77,25 @@ def test_prefill_whole_prompts_and_single_rows():
         err = float(np.max(np.abs(as_f64(out) - ref)))
         _say(f"prefill {qmode}: max abs err {err:.3e}")
         assert err <= TOL["bf16"]
+
+
+def test_prefill_work_order_many_pairs_and_ties():
+    """The bf16 launch deals (sequence, KV head) pairs to the XCDs and ranks
+    each XCD's pairs by length.  More than 64 pairs per XCD (80 sequences x
+    8 KV heads) takes the plain order; equal lengths everywhere are ties the
+    ranking breaks by index.  Every row must still be computed exactly once."""
+    rng = np.random.default_rng(307_366)
+    many = [int(x) for x in rng.integers(1, 50, size=80)]
+    cases = [("many pairs", many, [min(L, 7) for L in many], 8, 8, 64),
+             ("ties", [64] * 20, [64] * 20, 8, 2, 128),
+             ("ties, one KV head", [33] * 17 + [5] * 9, [9] * 17 + [5] * 9, 4, 1, 64)]
+    for name, lens, qlens, Hq, Hkv, D in cases:
+        w = W.prefill(lens, qlens, Hq, Hkv, D, 16, "bf16", seed=307_367)
+        out = run_prefill_gpu(w)
+        ref = oracle.run_prefill(w)["out"]
+        err = float(np.max(np.abs(as_f64(out) - ref)))
+        _say(f"prefill work order, {name}: {len(lens)} seqs x {Hkv} KV heads, max abs err {err:.3e}")
+        assert err <= TOL["bf16"], name
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
