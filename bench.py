@@ -400,6 +400,15 @@ def run_cp_bench(args):
     world, inter = args.cp_world, 1
     w = W_.llama3_8b_decode()
     B = w.block_size
+    # --partition 0: single pass (one launch, no merge).  By default a rank
+    # whose sequences hold 512 tokens or fewer on average runs single pass:
+    # on the 64-sequence layer split-KV won at W = 2 (52.0 against 62.8 us),
+    # tied at W = 4 (33.0 / 32.4) and lost at W = 8 (24.6 against 18.4), where
+    # its fixed cost (the record merge launch) outweighs the balance it buys.
+    P = args.partition
+    if P is None:
+        share = [-(-int(L) // (B * world)) * B for L in w.context_lens]  # tokens per rank, rounded up
+        P = 0 if float(np.mean(share)) <= 512 else 4096
     # the oracle computes the same result unsplit; its rate per KV byte does
     # not depend on which tokens a rank holds
     cpu = None if args.no_cpu_baseline else cpu_baseline(w)
@@ -431,7 +440,7 @@ def run_cp_bench(args):
         local = pa.cp_context_lens(cl, B, world, r, inter)
         mcl = int(local.max().item())
         ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl,
-                                4096, dev)
+                                P, dev) if P > 0 else None
         # the rank's pool in args.layers copies, rotated per step like the
         # decode bench, so K/V come from HBM rather than the last-level cache
         pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(args.layers - 1)]
@@ -443,7 +452,7 @@ def run_cp_bench(args):
     def rank_decode(r, i):
         pools, local, mcl, ws = ranks[r]
         kc, vc = pools[i % len(pools)]
-        pa.decode(q, kc, vc, bt, local, mcl, w.scale, partition_size=4096, workspace=ws,
+        pa.decode(q, kc, vc, bt, local, mcl, w.scale, partition_size=P, workspace=ws,
                   out=outs[r], lse=lses[r])
 
     def step(i):
@@ -477,10 +486,12 @@ def run_cp_bench(args):
         "config": {"workload": f"llama3_8b_decode over {world} context-parallel ranks",
                    "batch": w.num_seqs, "cp_world": world, "interleave": inter,
                    "layers_rotated": args.layers,
-                   "rank0_tokens": int(local0.sum()),
-                   "step": "per rank pa_decode_lse (partials + merge); pa_merge_states"},
+                   "rank0_tokens": int(local0.sum()), "partition_size": P,
+                   "step": "per rank pa_decode_lse (" + ("partials + merge" if P else "single pass")
+                           + "); pa_merge_states"},
         "rank_decode_us": round(rank_ms * 1e3, 3), "merge_states_us": round(merge_ms * 1e3, 3),
-        "roofline": {"kernel": "pa_decode_lse of rank 0 (decode + merge launches)", "bound": "hbm",
+        "roofline": {"kernel": "pa_decode_lse of rank 0 (" + ("decode + merge launches" if P else "one launch")
+                     + ")", "bound": "hbm",
                      "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "avg_us": round(rank_ms * 1e3, 3),
                      "bytes_per_launch": rank_bytes, "traffic": None},

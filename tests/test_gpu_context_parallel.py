@@ -199,17 +199,18 @@ def test_kernel_tables_from_allocator_tables(k, Bk):
     assert float(np.max(np.abs(as_f64(out) - ref))) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("P", [4096, 0])
 @pytest.mark.parametrize("world", [2, 4, 8])
-def test_full_llama3_8b_context_parallel(world):
+def test_full_llama3_8b_context_parallel(world, P):
     """The 64-sequence Llama-3-8B-shaped layer over W ranks, in the launch
     configuration the context-parallel benchmark times: one shared table of
     virtual blocks (B * W tokens, shuffled ids), interleave 1, one pool per
-    rank, pa_decode_lse with 4096-token partitions and a workspace, then
-    pa_merge_states.  Rank slots and local lengths bit for bit, the merged
+    rank, pa_decode_lse with 4096-token partitions and a workspace or in a
+    single pass, then pa_merge_states.  Rank slots and local lengths bit for bit, the merged
     output against the oracle's unsplit decode of every row."""
     w = W.llama3_8b_decode()
     B, inter = w.block_size, 1
-    _say(f"full cp decode W={world}: {w.num_seqs} seqs, lengths {int(w.context_lens.min())}.."
+    _say(f"full cp decode W={world} P={P}: {w.num_seqs} seqs, lengths {int(w.context_lens.min())}.."
          f"{int(w.context_lens.max())}")
     ref = oracle.run_step(w)["out"]
     nvb = [-(-int(L) // (B * world)) for L in w.context_lens]
@@ -238,9 +239,9 @@ def test_full_llama3_8b_context_parallel(world):
         ref_local = [oracle.cp_context_len(int(L), B, world, r, inter) for L in w.context_lens]
         assert local.cpu().tolist() == ref_local, r
         mcl = max(ref_local)
-        ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, 4096,
-                                "cuda")
-        pa.decode(q, k, v, bt, local, mcl, w.scale, partition_size=4096, workspace=ws,
+        ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, P,
+                                "cuda") if P else None
+        pa.decode(q, k, v, bt, local, mcl, w.scale, partition_size=P, workspace=ws,
                   out=outs[r], lse=lses[r])
         del k, v
     merged = pa.merge_states(outs, lses)
