@@ -68,7 +68,7 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
         "bytes": 297752750, "fetch_bytes": 230643886, "write_bytes": 67108864,
-        "sources_sha256": "e3a02c9d0010517eaf9e5f999a41826d9f119d647c8da9b0ef1567b7af65c240"},
+        "sources_sha256": "fdfa098cdc1eabe2d303da532c75f7b3f242b30025bf9982f0b08b11efb56142"},
 }
 
 
