@@ -144,43 +144,59 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(
 
   const int row_elems = num_kv_heads * head_dim;
   constexpr int kVec = 16 / sizeof(Elem);
-  // whole blocks, one (block, KV head) tile at a time
+  // Whole blocks: the (block, KV head) tiles of this workgroup (blocks that
+  // start at a listed row, heads y, y + gridDim.y, ...) go in rounds of as
+  // many tiles as the LDS area holds, so that a round's loads and stores are
+  // all in flight together: K rows straight to the tile, V rows into LDS as
+  // [token][dim], then out as [dim][token].
+  __shared__ int s_list[kWriteChunk];
+  __shared__ int s_count;
+  if (t == 0) s_count = 0;
+  __syncthreads();
+  if (s_start[t]) s_list[atomicAdd(&s_count, 1)] = t;
+  __syncthreads();
+  const int nstart = s_count;
   const int dvecs = head_dim / kVec;
-  for (int r = 0; r < n; ++r) {
-    if (!s_start[r]) continue;
-    const int64_t block = s_slot[r] / B;
-    for (int h = blockIdx.y; h < num_kv_heads; h += gridDim.y) {
-      const int64_t tile = (block * num_kv_heads + h) * int64_t(B) * head_dim;
-      // K: token j's head-h row is contiguous in the source and the tile
-      for (int v = t; v < B * dvecs; v += kThreads) {
-        const int j = v / dvecs;
-        const int dv = v % dvecs;
-        const Elem* src = key + (c0 + r + j) * row_elems + int64_t(h) * head_dim;
-        reinterpret_cast<uint4*>(k_cache + tile + int64_t(j) * head_dim)[dv] =
-            reinterpret_cast<const uint4*>(src)[dv];
-      }
-      // V: the B rows of head h into LDS as [token][dim], out as [dim][token]
-      for (int v = t; v < B * dvecs; v += kThreads) {
-        const int j = v / dvecs;
-        const int dv = v % dvecs;
-        const Elem* src = value + (c0 + r + j) * row_elems + int64_t(h) * head_dim;
-        reinterpret_cast<uint4*>(v_tile + j * head_dim)[dv] =
-            reinterpret_cast<const uint4*>(src)[dv];
-      }
-      __syncthreads();
-      const int jvecs = B / kVec;
-      for (int v = t; v < head_dim * jvecs; v += kThreads) {
-        const int d = v / jvecs;
-        const int j0 = (v % jvecs) * kVec;
-        Elem e[kVec];
-#pragma unroll
-        for (int u = 0; u < kVec; ++u) e[u] = v_tile[(j0 + u) * head_dim + d];
-        uint4 w;
-        __builtin_memcpy(&w, e, 16);
-        *reinterpret_cast<uint4*>(v_cache + tile + int64_t(d) * B + j0) = w;
-      }
-      __syncthreads();
+  const int jvecs = B / kVec;
+  const int heads_here = (num_kv_heads - int(blockIdx.y) + int(gridDim.y) - 1) / int(gridDim.y);
+  const int units = nstart * heads_here;
+  const int tile_elems = B * head_dim;
+  const int per_round = max(1, int(kTileLdsBytes / (int64_t(tile_elems) * sizeof(Elem))));
+  for (int u0 = 0; u0 < units; u0 += per_round) {
+    const int nb = min(per_round, units - u0);
+    for (int v = t; v < nb * B * dvecs; v += kThreads) {
+      const int ui = v / (B * dvecs);
+      const int w = v % (B * dvecs);
+      const int j = w / dvecs;
+      const int dv = w % dvecs;
+      const int unit = u0 + ui;
+      const int r = s_list[unit / heads_here];
+      const int h = int(blockIdx.y) + (unit % heads_here) * int(gridDim.y);
+      const int64_t tile = (s_slot[r] / B * num_kv_heads + h) * int64_t(tile_elems);
+      const int64_t src = (c0 + r + j) * row_elems + int64_t(h) * head_dim;
+      reinterpret_cast<uint4*>(k_cache + tile + int64_t(j) * head_dim)[dv] =
+          reinterpret_cast<const uint4*>(key + src)[dv];
+      reinterpret_cast<uint4*>(v_tile + (ui * B + j) * head_dim)[dv] =
+          reinterpret_cast<const uint4*>(value + src)[dv];
     }
+    __syncthreads();
+    for (int v = t; v < nb * head_dim * jvecs; v += kThreads) {
+      const int ui = v / (head_dim * jvecs);
+      const int w = v % (head_dim * jvecs);
+      const int d = w / jvecs;
+      const int j0 = (w % jvecs) * kVec;
+      const int unit = u0 + ui;
+      const int r = s_list[unit / heads_here];
+      const int h = int(blockIdx.y) + (unit % heads_here) * int(gridDim.y);
+      const int64_t tile = (s_slot[r] / B * num_kv_heads + h) * int64_t(tile_elems);
+      Elem e[kVec];
+#pragma unroll
+      for (int u = 0; u < kVec; ++u) e[u] = v_tile[(ui * B + j0 + u) * head_dim + d];
+      uint4 q;
+      __builtin_memcpy(&q, e, 16);
+      *reinterpret_cast<uint4*>(v_cache + tile + int64_t(d) * B + j0) = q;
+    }
+    __syncthreads();
   }
 
   // the other rows, one wave per row
@@ -259,7 +275,8 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const 
                         block_size <= kWriteChunk;
   // Few chunks (a prefill chunk, a decode step): split each chunk's heads
   // over workgroups so the write has enough of them; 8192 rows of 8 heads
-  // took 240 us as 32 workgroups and 71 us as 256.  Many chunks (a whole
+  // took 240 us as 32 workgroups and 71 us as 256, then 47.5 us once
+  // each workgroup moved its tiles in rounds.  Many chunks (a whole
   // history) fill the device already, and one pass over all heads of a chunk
   // measured faster there (131,759 rows: 337 us against 381 us split).
   const int chunks = ceil_div(num_tokens, kWriteChunk);
