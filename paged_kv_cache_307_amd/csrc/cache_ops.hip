@@ -69,8 +69,14 @@ __device__ __forceinline__ void store_row(Elem* __restrict__ k_cache, Elem* __re
   }
 }
 
-// Rows per workgroup of the write.
+// Rows per workgroup of the write (the LDS arrays are sized for it, one row
+// per thread).  Writes with few chunks take 64 rows per workgroup and split
+// the KV heads over workgroups: a prefill chunk's 8192 rows of 8 heads in
+// 1024 workgroups, 25.9 us, against 30.8 us at 128 rows and 47 us at 256.
+// A whole history keeps 256 rows and one pass over all heads of a chunk:
+// 331 us for 131,759 rows, against 369 us in 64-row split chunks.
 constexpr int kWriteChunk = 256;
+constexpr int kSmallWriteChunk = 64;
 // Below this many chunks the write also splits KV heads over workgroups.
 constexpr int kSplitHeadsBelowChunks = 512;
 // Largest (block, KV head) V tile the write transposes through LDS.
@@ -95,7 +101,7 @@ __device__ __forceinline__ void store_head_wave(Elem* __restrict__ k_cache,
   for (int d = lane; d < head_dim; d += 64) vt[int64_t(d) * block_size] = src_v[d];  // [d][off]
 }
 
-// The write of rows [c0, c0 + n) of a slot mapping, n <= kWriteChunk.
+// The write of rows [c0, c0 + n) of a slot mapping, n <= CHUNK <= kWriteChunk.
 //
 // Rows usually come sequence by sequence with ascending positions, so most
 // blocks receive all B of their slots, in order, from B consecutive rows.
@@ -110,7 +116,7 @@ __device__ __forceinline__ void store_head_wave(Elem* __restrict__ k_cache,
 // The grid's second dimension splits the KV heads: workgroup (c, y) writes
 // heads y, y + gridDim.y, ... of chunk c, so a chunk's blocks are written by
 // as many workgroups as there are heads.
-template <typename Elem>
+template <typename Elem, int CHUNK>
 __global__ __launch_bounds__(kThreads) void write_kv_kernel(
     Elem* __restrict__ k_cache, Elem* __restrict__ v_cache, const Elem* __restrict__ key,
     const Elem* __restrict__ value, const int64_t* __restrict__ slots, int num_tokens,
@@ -118,8 +124,9 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(
   __shared__ int64_t s_slot[kWriteChunk];
   __shared__ int s_start[kWriteChunk];  // row r starts a block this chunk fills
   __shared__ __align__(16) Elem v_tile[kTileLdsBytes / sizeof(Elem)];
-  const int64_t c0 = int64_t(blockIdx.x) * kWriteChunk;
-  const int n = int(min<int64_t>(kWriteChunk, num_tokens - c0));
+  static_assert(CHUNK <= kWriteChunk && kWriteChunk == kThreads, "one slot per thread");
+  const int64_t c0 = int64_t(blockIdx.x) * CHUNK;
+  const int n = int(min<int64_t>(CHUNK, num_tokens - c0));
   const int t = threadIdx.x;
   const int64_t limit = int64_t(num_blocks) * block_size;
   {
@@ -164,6 +171,7 @@ __global__ __launch_bounds__(kThreads) void write_kv_kernel(
   const int per_round = max(1, int(kTileLdsBytes / (int64_t(tile_elems) * sizeof(Elem))));
   for (int u0 = 0; u0 < units; u0 += per_round) {
     const int nb = min(per_round, units - u0);
+#pragma unroll 4
     for (int v = t; v < nb * B * dvecs; v += kThreads) {
       const int ui = v / (B * dvecs);
       const int w = v % (B * dvecs);
@@ -272,23 +280,27 @@ hipError_t launch_write_kv(void* k_cache, void* v_cache, const void* key, const 
                          (reinterpret_cast<uintptr_t>(value) % 16 == 0);
   const int tile_path = v_aligned && (int64_t(block_size) * elem_bytes % 16 == 0) &&
                         int64_t(block_size) * head_dim * elem_bytes <= kTileLdsBytes &&
-                        block_size <= kWriteChunk;
+                        block_size <= kSmallWriteChunk;
   // Few chunks (a prefill chunk, a decode step): split each chunk's heads
   // over workgroups so the write has enough of them; 8192 rows of 8 heads
   // took 240 us as 32 workgroups and 71 us as 256, then 47.5 us once
-  // each workgroup moved its tiles in rounds.  Many chunks (a whole
-  // history) fill the device already, and one pass over all heads of a chunk
-  // measured faster there (131,759 rows: 337 us against 381 us split).
-  const int chunks = ceil_div(num_tokens, kWriteChunk);
-  const int split = chunks >= kSplitHeadsBelowChunks ? 1 : (num_kv_heads < 65535 ? num_kv_heads : 65535);
+  // each workgroup moved its tiles in rounds, 25.9 us in 64-row chunks.
+  // Many chunks (a whole history) fill the device already, and one pass
+  // over all heads of a chunk measured faster there.
+  const bool many = ceil_div(num_tokens, kWriteChunk) >= kSplitHeadsBelowChunks;
+  const int chunk = many ? kWriteChunk : kSmallWriteChunk;
+  const int chunks = ceil_div(num_tokens, chunk);
+  const int split = many ? 1 : (num_kv_heads < 65535 ? num_kv_heads : 65535);
   const dim3 grid{unsigned(chunks), unsigned(split)};
   if (elem_bytes == 4) {
-    return launch(write_kv_kernel<uint32_t>, grid, dim3(kThreads), 0, stream,
+    auto k = many ? write_kv_kernel<uint32_t, kWriteChunk> : write_kv_kernel<uint32_t, kSmallWriteChunk>;
+    return launch(k, grid, dim3(kThreads), 0, stream,
                   static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
                   static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value), slots,
                   num_tokens, num_kv_heads, head_dim, block_size, num_blocks, tile_path);
   }
-  return launch(write_kv_kernel<uint16_t>, grid, dim3(kThreads), 0, stream,
+  auto k = many ? write_kv_kernel<uint16_t, kWriteChunk> : write_kv_kernel<uint16_t, kSmallWriteChunk>;
+  return launch(k, grid, dim3(kThreads), 0, stream,
                 static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
                 static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value), slots,
                 num_tokens, num_kv_heads, head_dim, block_size, num_blocks, tile_path);
