@@ -49,6 +49,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 1;  // waves per workgroup: 1, 2, 4 -> 445, 442, 438 us on the chunked layer, 470, 483, 496 on whole 2048-token prompts
 constexpr int kTile = 16;
@@ -119,10 +120,13 @@ __device__ __forceinline__ SeqRows seq_rows(const PrefillArgs& a, int s, int B) 
   return r;
 }
 
+// K as the QK product's operand (lane: token l % 16, dims 32j + 8 (l / 16)
+// .. +7); V as the 32 x 32 PV product's operand: lane l holds dim 32b + l %
+// 32 and tokens 8 (l / 32) .. +7 of the tile, one 16-byte load per block.
 template <int D>
 struct KVTile {
   uint4 k[D / 32];
-  uint2 v[D / 16];
+  uint4 v[D / 32];
 };
 
 // Loads of the 16-token tile at t0 of KV head kvh (ids of its block(s) in
@@ -151,13 +155,13 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(vc + tile + in_block * 2), 0, int(kTileBytes), kRawWord3);
     const int k_off = col * D * 2 + grp * 16;
-    const int v_off = col * B * 2 + grp * 8;
+    const int v_off = (lane & 31) * B * 2 + (lane >> 5) * 16;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j)
       r.k[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off, 64 * j, 0));
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      r.v[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, v_off, 32 * B * c, 0));
+    for (int b = 0; b < D / 32; ++b)
+      r.v[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off, 64 * B * b, 0));
     // A bad block id poisons the tile's K with NaN, so the products carry
     // it into every logit of the tile (rare; the branch is wave-uniform).
     if (__builtin_amdgcn_readfirstlane(int(bad0))) {
@@ -165,19 +169,20 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
       for (int j = 0; j < D / 32; ++j) r.k[j] = make_uint4(kNanPair, kNanPair, kNanPair, kNanPair);
     }
   } else {
+    // K row `col` and V tokens 8 (l / 32) .. +7 (a whole 8-token dim row)
+    // come from the tile's first or second block
     const bool k_second = col >= B;
-    const bool v_second = grp >= 2;
+    const bool v_second = (lane >> 5) != 0;
     const int kr = k_second ? col - B : col;
-    const int vt = 4 * grp - (v_second ? B : 0);
     const char* kb = kc + (int64_t(k_second ? pb1 : pb0) * a.num_kv_heads + kvh) * kTileBytes +
                      int64_t(kr) * D * 2 + grp * 16;
     const char* vb = vc + (int64_t(v_second ? pb1 : pb0) * a.num_kv_heads + kvh) * kTileBytes +
-                     (int64_t(col) * B + vt) * 2;
+                     int64_t(lane & 31) * B * 2;
 #pragma unroll
     for (int j = 0; j < D / 32; ++j) r.k[j] = *reinterpret_cast<const uint4*>(kb + 64 * j);
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      r.v[c] = *reinterpret_cast<const uint2*>(vb + int64_t(32) * B * c);
+    for (int b = 0; b < D / 32; ++b)
+      r.v[b] = *reinterpret_cast<const uint4*>(vb + int64_t(64) * B * b);
     // K row `col` comes from the block of token `col`; a bad id there
     // poisons that token's logits in every column
     if (k_second ? bad1 : bad0) {
@@ -188,13 +193,22 @@ __device__ __forceinline__ void load_kv_tile(KVTile<D>& r, const PrefillArgs& a,
   }
 }
 
+// a for lanes 0-15 and 32-47, b for lanes 16-31 and 48-63.  The empty asm
+// hands the compiler two register values, so that the choice stays a lane
+// select; picking between two elements of a register array by lane was
+// otherwise turned into a load through a lane-dependent address, which put
+// the array in scratch memory.
+__device__ __forceinline__ float pick_half(int lane, float a, float b) {
+  asm("" : "+v"(a), "+v"(b));
+  return (lane & 16) ? b : a;
+}
+
 // NC: 16-row column tiles per wave (each K/V tile feeds NC products of each
 // kind); RING: register tiles in flight (tile k + RING - 1 loads while tile
 // k is consumed).
 template <int D, int B, int NC, int RING>
 __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillArgs a) {
   constexpr int KSTEPS = D / 32;
-  constexpr int DCH = D / 16;
   constexpr int kWaveRows = kTile * NC;
   const int G = a.group;
   const int lane = threadIdx.x & 63;
@@ -255,7 +269,11 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
     qh[c] = kvh * G + row % G;
   }
 
-  floatx4_t acc[NC][DCH];
+  // O^T accumulators of the 32 x 32 PV products: column pair p holds column
+  // tiles 2p and 2p + 1; lane l's column is tile 2p + (l / 16) % 2, row
+  // l % 16; element e is dim 32b + 8 (e / 4) + 4 (l / 32) + e % 4.
+  static_assert(NC % 2 == 0, "column tiles go in pairs");
+  floatx16_t acc[NC / 2][D / 32];
   // m_run: the maximum in use (of c q.k, c = |scale| log2 e, see cpos).  Kept beside
   // it, since they change only when m_run does: neg_m = -m_run, or 0 while
   // the column has seen nothing (m_run = -inf), the exponent's offset; and
@@ -265,7 +283,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
 #pragma unroll
-    for (int d = 0; d < DCH; ++d) acc[c][d] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < D / 32; ++b)
+      if (c < NC / 2) acc[c][b] = floatx16_t{};
     m_run[c] = -INFINITY;
     l_run[c] = 0.f;
     neg_m[c] = 0.f;
@@ -325,13 +344,17 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
       const int t0 = k * kTile;
       const int tb = t0 + 4 * grp;
       if (t0 + kTile > t_end) {  // tokens past the wave's range may be unused slots
-        const int nv = min(max(t_end - tb, 0), 4);
-        const uint32_t mx = (nv >= 1 ? 0x0000FFFFu : 0u) | (nv >= 2 ? 0xFFFF0000u : 0u);
-        const uint32_t my = (nv >= 3 ? 0x0000FFFFu : 0u) | (nv >= 4 ? 0xFFFF0000u : 0u);
+        const int nv = min(max(t_end - (t0 + 8 * (lane >> 5)), 0), 8);  // this lane's V tokens
+        uint32_t m4[4];
 #pragma unroll
-        for (int d = 0; d < DCH; ++d) {
-          r.v[d].x &= mx;
-          r.v[d].y &= my;
+        for (int q = 0; q < 4; ++q)
+          m4[q] = (nv > 2 * q ? 0x0000FFFFu : 0u) | (nv > 2 * q + 1 ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b) {
+          r.v[b].x &= m4[0];
+          r.v[b].y &= m4[1];
+          r.v[b].z &= m4[2];
+          r.v[b].w &= m4[3];
         }
       }
       // wave-uniform: a scalar branch skips the masks on interior tiles
@@ -371,16 +394,21 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
         grow |= tmax[c] > thr[c];
       }
       if (__any(grow)) {  // rare: one branch for all column tiles
+        float alpha[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const float m_new = fmaxf(m_run[c], tmax[c] * cpos);
-          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
-          l_run[c] *= alpha;
-#pragma unroll
-          for (int d = 0; d < DCH; ++d) acc[c][d] *= alpha;
+          alpha[c] = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[c] - m_new);
+          l_run[c] *= alpha[c];
           m_run[c] = m_new;
           neg_m[c] = m_new == -INFINITY ? 0.f : -m_new;
           thr[c] = (m_new + kRescale) * inv_c;
+        }
+#pragma unroll
+        for (int p = 0; p < NC / 2; ++p) {
+          const float al = pick_half(lane, alpha[2 * p], alpha[2 * p + 1]);
+#pragma unroll
+          for (int b = 0; b < D / 32; ++b) acc[p][b] *= al;
         }
       }
       short4_t pop[NC];
@@ -393,12 +421,22 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
         pop[c] = __builtin_bit_cast(short4_t,
                                     make_uint2(pack2_rne(pr[0], pr[1]), pack2_rne(pr[2], pr[3])));
       }
+      // P^T of column tiles 2p, 2p + 1 as the 32 x 32 product's operand:
+      // lane l needs tokens 8 (l / 32) .. +7 of its column, which sit in
+      // lanes l and l + 16 (first tile) or l - 16 and l (second tile); one
+      // lane swap between 16-lane rows per 32-bit word brings them there.
 #pragma unroll
-      for (int d = 0; d < DCH; ++d)
+      for (int p = 0; p < NC / 2; ++p) {
+        const uint2 pa = __builtin_bit_cast(uint2, pop[2 * p]);
+        const uint2 pb = __builtin_bit_cast(uint2, pop[2 * p + 1]);
+        const auto s0 = __builtin_amdgcn_permlane16_swap(pa.x, pb.x, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(pa.y, pb.y, false, false);
+        const bf16x8_t pp = __builtin_bit_cast(bf16x8_t, u32x4_t{s0[0], s1[0], s0[1], s1[1]});
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
-          acc[c][d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(short4_t, r.v[d]), pop[c], acc[c][d], 0, 0, 0);
+        for (int b = 0; b < D / 32; ++b)
+          acc[p][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, r.v[b]), pp,
+                                                              acc[p][b], 0, 0, 0);
+      }
     };
 
     // Ring of RING register tiles; every load is issued unconditionally (the
@@ -434,23 +472,30 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
     }
   }
 
+  float l_tot[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const float l_tot = col_sum(l_run[c]);
-    if (col_ok[c] && a.lse && grp == 0) {
-      // ln sum_t e^(scale q.k_t) = (m + log2 l) ln 2, m and l in the log2 domain
-      a.lse[int64_t(q0 + qi[c]) * a.num_heads + qh[c]] =
-          l_tot > 0.f ? (m_run[c] + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-    }
-    if (col_ok[c]) {
-      const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // a row that sees no token: zeros
-      uint16_t* o = static_cast<uint16_t*>(a.out) +
-                    (int64_t(q0 + qi[c]) * a.num_heads + qh[c]) * D + 4 * grp;
+  for (int c = 0; c < NC; ++c) l_tot[c] = col_sum(l_run[c]);
+  // lane l writes row r0 + 32p + l % 32 (column tile 2p + (l / 16) % 2),
+  // dims 32b + 8i + 4 (l / 32) .. +3
 #pragma unroll
-      for (int d = 0; d < DCH; ++d)
-        *reinterpret_cast<uint2*>(o + 16 * d) =
-            make_uint2(pack2_rne(acc[c][d][0] * inv_l, acc[c][d][1] * inv_l),
-                       pack2_rne(acc[c][d][2] * inv_l, acc[c][d][3] * inv_l));
+  for (int p = 0; p < NC / 2; ++p) {
+    const float lt = pick_half(lane, l_tot[2 * p], l_tot[2 * p + 1]);
+    const float mr = pick_half(lane, m_run[2 * p], m_run[2 * p + 1]);
+    const int row = r0 + 32 * p + (lane & 31);
+    if (row < nrows) {
+      const int64_t orow = int64_t(q0 + row / G) * a.num_heads + kvh * G + row % G;
+      if (a.lse && lane < 32)
+        // ln sum_t e^(scale q.k_t) = (m + log2 l) ln 2, m and l in the log2 domain
+        a.lse[orow] = lt > 0.f ? (mr + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
+      const float inv_l = lt > 0.f ? 1.0f / lt : 0.f;  // a row that sees no token: zeros
+      uint16_t* o = static_cast<uint16_t*>(a.out) + orow * D + 4 * (lane >> 5);
+#pragma unroll
+      for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint2*>(o + 32 * b + 8 * i) =
+              make_uint2(pack2_rne(acc[p][b][4 * i] * inv_l, acc[p][b][4 * i + 1] * inv_l),
+                         pack2_rne(acc[p][b][4 * i + 2] * inv_l, acc[p][b][4 * i + 3] * inv_l));
     }
   }
 }
