@@ -67,8 +67,8 @@ PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_30
                    "paged_kv_cache_307_amd/build.py"]
 PREFILL_TRAFFIC = {
     "llama3_8b_prefill": {
-        "bytes": 297752750, "fetch_bytes": 230643886, "write_bytes": 67108864,
-        "sources_sha256": "fdfa098cdc1eabe2d303da532c75f7b3f242b30025bf9982f0b08b11efb56142"},
+        "bytes": 297528224, "fetch_bytes": 230396448, "write_bytes": 67131776,
+        "sources_sha256": "5a0f4639d7762fb380971ef827c03c6c31c8134098f6c04ba437579488ed8dd8"},
 }
 
 
@@ -374,7 +374,7 @@ def run_prefill_bench(args):
         "query_tokens_per_s": round(w.num_query_tokens / (ms_per_step * 1e-3), 1),
         "flops_per_step": F,
         "roofline": {
-            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 1 wave per workgroup, Q in LDS (pa_prefill)", "bound": "mfma",
+            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 1 wave per workgroup, Q in LDS, P.V on 32x32x16 (pa_prefill)", "bound": "mfma",
             "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_us": round(attend_ms * 1e3, 3),
             "flops_per_launch": F, "traffic": prefill_traffic(w.name),
