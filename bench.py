@@ -88,13 +88,42 @@ def make_workload(name):
     return make(), partition
 
 
-def algorithmic_bytes(w):
+def unique_kv_tokens(w):
+    """Distinct cache slots the step reads: over every physical block in use,
+    the most tokens any sequence reads from it (a sequence reads a block's
+    slots 0 .. n-1).  Equal to the sum of context lengths when no block is
+    shared; a block shared by a group of sequences (the pages' reference-
+    counted prefix) counts once."""
+    B = w.block_size
+    ids, n = [], []
+    for s, L in enumerate(w.context_lens):
+        L = int(L)
+        nb = -(-L // B)
+        if nb == 0:
+            continue
+        ids.append(w.block_tables[s, :nb].astype(np.int64))
+        fill = np.full(nb, B, np.int64)
+        fill[-1] = L - (nb - 1) * B
+        n.append(fill)
+    if not ids:
+        return 0
+    ids, n = np.concatenate(ids), np.concatenate(n)
+    most = np.zeros(int(ids.max()) + 1, np.int64)
+    np.maximum.at(most, ids, n)
+    return int(most.sum())
+
+
+def algorithmic_bytes(w, unique=True):
     """Bytes one step must move at minimum: K and V of the live tokens read
     once (the step's own row included), q, out, the table entries in use, the
-    context lengths, and the step's K/V rows stored to the cache."""
+    context lengths, and the step's K/V rows stored to the cache.  With
+    ``unique`` a slot read by several sequences (a shared prefix block) counts
+    once: that is what HBM must deliver, and what a roofline fraction is taken
+    on.  Without it every sequence's reads count (logical bytes)."""
     e = w.elem_bytes
     L = w.context_lens.astype(np.int64)
-    kv = int(L.sum()) * w.num_kv_heads * w.head_dim * 2 * e
+    tokens = unique_kv_tokens(w) if unique else int(L.sum())
+    kv = tokens * w.num_kv_heads * w.head_dim * 2 * e
     q = w.num_seqs * w.num_heads * w.head_dim * e
     table = int(sum(-(-int(x) // w.block_size) for x in L)) * 4
     # copy-on-write before the step (the shared-prefix fork step): each pair
@@ -143,39 +172,134 @@ def measured_traffic(workload, partition, append, shared):
     return rec["bytes"]
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """The oracle (fp64 NumPy, as it is) on this host: one full step
-    (write + decode) of the same workload, repeated until ~budget_s."""
+# The CPU baseline's state, set before its worker processes fork so that
+# they share it (pools in shared memory: the parent's per-step writes and
+# copies are what the workers read).
+_CPU = {}
+
+
+def _shared_like(a):
+    """A copy of array ``a`` in anonymous shared memory (inherited by forked
+    workers, writes visible both ways)."""
+    import mmap
+    buf = mmap.mmap(-1, max(a.nbytes, 1))
+    out = np.frombuffer(buf, dtype=a.dtype, count=a.size).reshape(a.shape)
+    out[...] = a
+    return out
+
+
+def _cpu_decode_units(units):
+    """Worker: the oracle's decode of (sequence, [KV heads]) units; returns
+    the rows it computed."""
+    import oracle
+    st = _CPU
+    w = st["w"]
+    G = w.num_heads // w.num_kv_heads
+    got = []
+    for s, heads in units:
+        out = oracle.decode(st["q"], st["k"], st["v"], w.block_tables, w.context_lens, w.scale,
+                            w.num_kv_heads, w.block_size, w.dtype, seqs=[s], kv_heads=heads)
+        got.append((s, heads, np.stack([out[s, g * G:(g + 1) * G] for g in heads])))
+    return got
+
+
+def _cpu_worker_init():
+    from threadpoolctl import threadpool_limits
+    # one BLAS thread per worker process, kept for the worker's life
+    _CPU["limits"] = threadpool_limits(limits=1)
+
+
+def _split_units(w, n):
+    """(sequence, KV head) units cut into n contiguous ranges of about equal
+    tokens, each as a list of (sequence, [KV heads]) runs."""
+    units = [(s, g) for s in range(w.num_seqs) for g in range(w.num_kv_heads)]
+    cost = np.array([max(int(w.context_lens[s]), 1) for s, _ in units], np.float64)
+    cum = np.cumsum(cost)
+    cuts = np.searchsorted(cum, cum[-1] * np.arange(1, n) / n)
+    chunks = []
+    for part in np.split(np.arange(len(units)), cuts):
+        runs = []
+        for i in part:
+            s, g = units[i]
+            if runs and runs[-1][0] == s:
+                runs[-1][1].append(g)
+            else:
+                runs.append((s, [g]))
+        if runs:
+            chunks.append(runs)
+    return chunks
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers():
+    """Worker processes for the CPU baseline: the host cores this process may
+    run on, at most 16 (one GPU's share of a shared host)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def cpu_baseline(w, cpu_seconds=24.0):
+    """The oracle (fp64 NumPy, as it is) on this host's cores: full steps of
+    the same workload (copies if any, write, decode), the decode's (sequence,
+    KV head) units spread over a pool of worker processes with one BLAS
+    thread each, repeated for about ``cpu_seconds`` of CPU time in all."""
+    import multiprocessing as mp
+
     from threadpoolctl import threadpool_limits
 
     import oracle
     B = w.block_size
+    n = cpu_workers()
     with threadpool_limits(limits=1):
         k_pool, v_pool = oracle.new_pools(w.num_blocks, w.num_kv_heads, B, w.head_dim, w.dtype)
         hs = oracle.slot_mapping(w.hist_block_tables, w.hist_seq, w.hist_pos, B)
         oracle.write_kv(k_pool, v_pool, oracle.to_bits(w.hist_key, w.dtype),
                         oracle.to_bits(w.hist_value, w.dtype), hs, B)
-        q = oracle.to_bits(w.q, w.dtype)
+    _CPU.clear()
+    _CPU.update(w=w, q=oracle.to_bits(w.q, w.dtype), k=_shared_like(k_pool), v=_shared_like(v_pool))
+    del k_pool, v_pool
+    chunks = _split_units(w, n)
+    new_k, new_v = oracle.to_bits(w.new_key, w.dtype), oracle.to_bits(w.new_value, w.dtype)
+    budget = max(cpu_seconds / n, 1.0)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(n, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_worker_init_probe, range(n))  # every worker started before timing
         reps, t0 = 0, time.perf_counter()
         while True:
-            oracle.copy_blocks(k_pool, v_pool, w.copy_pairs)  # the fork step's copies (if any)
+            oracle.copy_blocks(_CPU["k"], _CPU["v"], w.copy_pairs)  # the fork step's copies
             ns = oracle.slot_mapping(w.block_tables, w.new_seq, w.new_pos, B)
-            oracle.write_kv(k_pool, v_pool, oracle.to_bits(w.new_key, w.dtype),
-                            oracle.to_bits(w.new_value, w.dtype), ns, B)
-            oracle.decode(q, k_pool, v_pool, w.block_tables, w.context_lens, w.scale,
-                          w.num_kv_heads, B, w.dtype)
+            oracle.write_kv(_CPU["k"], _CPU["v"], new_k, new_v, ns, B)
+            parts = pool.map(_cpu_decode_units, chunks)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 50:
+            if el >= budget or reps >= 50:
                 break
+    assert sum(len(p) for p in parts) == sum(len(c) for c in chunks)
+    _CPU.clear()
     step_s = el / reps
     ab = algorithmic_bytes(w)
     step_bytes = sum(ab.values())
-    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "tokens_per_s": round(w.num_seqs / step_s, 2),
-            "sample": f"{reps} full steps (copies if any, write + decode, all {w.num_seqs} "
-                      f"sequences) of the same workload, single thread, {el:.1f} s",
+    return {"value": round(step_bytes / step_s / 1e9, 4), "unit": "GB/s", "cores": n,
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "tokens_per_s": round(w.num_seqs / step_s, 2),
+            "sample": f"{reps} full steps (copies if any, write + decode of all {w.num_seqs} "
+                      f"sequences) of the same workload, {el:.1f} s wall; the decode's "
+                      f"(sequence, KV head) units over {n} worker processes, one BLAS thread "
+                      f"each; copies and writes in the parent, pools in shared memory",
             "block_manager_us_per_step": model_block_manager_timing(w)}
+
+
+def _cpu_worker_init_probe(_):
+    return os.getpid()
 
 
 def model_block_manager_timing(w, steps=50):
@@ -640,14 +764,20 @@ def main():
         copy_us = round(ev0.elapsed_time(ev1) / args.steps * 1e3, 3)
 
     ms_per_step = elapsed * 1e3 / args.steps
+    # unique bytes (a shared block counts once) set `value` and the roofline
+    # fraction; logical bytes (every sequence's reads) are reported beside
     ab = algorithmic_bytes(w)
+    ab_logical = algorithmic_bytes(w, unique=False)
     step_bytes = sum(ab.values())
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
-    # the timed kernel: reads K/V, q, table entries and lengths; in the
-    # appending step it also stores the rows (the merge writes most of out)
-    part_bytes = ab["kv"] + ab["q"] + ab["table"] + ab["context_lens"]
-    if not args.separate_write:
-        part_bytes += ab["write"]
+
+    def kernel_bytes(b):
+        # the timed kernel: reads K/V, q, table entries and lengths; in the
+        # appending step it also stores the rows (the merge writes most of out)
+        return b["kv"] + b["q"] + b["table"] + b["context_lens"] + \
+            (0 if args.separate_write else b["write"])
+
+    part_bytes = kernel_bytes(ab)
     part_gbs = part_bytes / (part_avg_ms * 1e-3) / 1e9
     L = w.context_lens
     rec = {
@@ -678,6 +808,8 @@ def main():
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "algorithmic_bytes_per_step": step_bytes,
+        "logical_bytes_per_step": sum(ab_logical.values()),
+        "logical_gbs": round(sum(ab_logical.values()) / (ms_per_step * 1e-3) / 1e9, 2),
         "copy_blocks_us": copy_us,
         "capacity": capacity_figures(w),
         "roofline": {
@@ -688,7 +820,11 @@ def main():
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(part_avg_ms * 1e3, 3), "per_launch_us": launch_pct,
             "bytes_per_launch": part_bytes,
+            "logical_bytes_per_launch": kernel_bytes(ab_logical),
             "traffic": measured_traffic(w.name, P, not args.separate_write, shared),
+            "traffic_source": "rocprofv3 FETCH_SIZE and WRITE_SIZE passes of this workload's "
+                              "step, recorded for the current kernel sources (null once they "
+                              "change)",
         },
         "cpu_baseline": cpu,
         "host_block_manager": host_block_manager_timing(w),

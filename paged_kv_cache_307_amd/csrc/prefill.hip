@@ -485,8 +485,11 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_bf16_mfma_kernel(PrefillA
     if (row < nrows) {
       const int64_t orow = int64_t(q0 + row / G) * a.num_heads + kvh * G + row % G;
       if (a.lse && lane < 32)
-        // ln sum_t e^(scale q.k_t) = (m + log2 l) ln 2, m and l in the log2 domain
-        a.lse[orow] = lt > 0.f ? (mr + __log2f(lt)) * 0.6931471805599453f : -INFINITY;
+        // ln sum_t e^(scale q.k_t) = (m + log2 l) ln 2, m and l in the log2 domain;
+        // -inf for a row that sees no token (l == 0), NaN for a row poisoned
+        // by a bad block id (l is NaN), so a merge of ranks propagates it
+        a.lse[orow] = lt > 0.f ? (mr + __log2f(lt)) * 0.6931471805599453f
+                               : (lt == 0.f ? -INFINITY : __builtin_nanf(""));
       const float inv_l = lt > 0.f ? 1.0f / lt : 0.f;  // a row that sees no token: zeros
       uint16_t* o = static_cast<uint16_t*>(a.out) + orow * D + 4 * (lane >> 5);
 #pragma unroll
@@ -547,7 +550,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a, int B) {
   float* o = static_cast<float*>(a.out) + (int64_t(sr.q0 + i) * a.num_heads + h) * D;
   const float inv_l = l > 0.f ? 1.0f / l : 0.f;
   if (a.lse && lane == 0)
-    a.lse[int64_t(sr.q0 + i) * a.num_heads + h] = l > 0.f ? m + logf(l) : -INFINITY;
+    a.lse[int64_t(sr.q0 + i) * a.num_heads + h] =
+        l > 0.f ? m + logf(l) : (l == 0.f ? -INFINITY : __builtin_nanf(""));  // NaN: bad block id
 #pragma unroll
   for (int e = 0; e < E; ++e) o[lane + 64 * e] = acc[e] * inv_l;
 }

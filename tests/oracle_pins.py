@@ -291,10 +291,43 @@ def check_bf16_widening(o):
     assert np.array_equal(o.widen(f.view(np.uint32), "f32"), f.astype(np.float64))
 
 
+# ---------------------------------------------------------------- capacity
+
+def check_kv_bytes(o):
+    """P3's KV-size estimate (section on why KV becomes a memory problem):
+    the bytes must be what the cache really stores.  Pin: write one token
+    through ``write_kv`` into fresh pools of one-slot blocks and count the
+    bytes that change; that is the size of one token in one layer.  The
+    estimate must equal it for K and V rows of both element types, and grow
+    linearly in layers and in tokens (the page's two conclusions: linear in
+    token count and in concurrent requests).  The page's own example, a
+    2048-token prompt with 512 generated tokens, then needs 2560 tokens'
+    worth per layer."""
+    markers = {"f32": 0x11223344, "bf16": 0x1234}  # every byte differs from the pool poison
+    for dtype, elem in (("f32", 4), ("bf16", 2)):
+        for Hkv, D in ((1, 4), (2, 64), (8, 128)):
+            k, v = o.new_pools(3, Hkv, 1, D, dtype)
+            k0, v0 = k.copy(), v.copy()
+            sd = k.dtype
+            row = np.full((1, Hkv, D), markers[dtype], dtype=sd)
+            o.write_kv(k, v, row, row, np.array([1], np.int64), 1)
+            changed = int(np.count_nonzero(k.view(np.uint8) != k0.view(np.uint8)) +
+                          np.count_nonzero(v.view(np.uint8) != v0.view(np.uint8)))
+            assert changed == 2 * Hkv * D * elem  # both rows were written whole
+            one = o.kv_bytes(1, 1, Hkv, D, elem)
+            assert one == changed
+            for layers, tokens in ((1, 7), (32, 1), (32, 2560), (3, 5)):
+                assert o.kv_bytes(layers, tokens, Hkv, D, elem) == layers * tokens * changed
+    ex = _golden("capacity_numbers.json")["context_example"]
+    assert ex["prompt"] + ex["generated"] == ex["context"]
+    per_layer = o.kv_bytes(1, ex["context"], 8, 128, 2)
+    assert per_layer == o.kv_bytes(1, ex["prompt"], 8, 128, 2) + o.kv_bytes(1, ex["generated"], 8, 128, 2)
+
+
 ALL_CHECKS = [
     check_bf16_widening,
     check_worked_example, check_block_counts, check_tiny_closed_form, check_slot_roundtrip,
     check_write_layout, check_paged_equals_unpaged, check_numpy_equals_brute,
     check_permutation_invariance, check_closed_forms, check_gqa_grouping,
-    check_empty_sequence, check_copy_on_write,
+    check_empty_sequence, check_copy_on_write, check_kv_bytes,
 ]

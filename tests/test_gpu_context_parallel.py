@@ -94,6 +94,58 @@ def test_context_parallel_decode(dt, world, inter, B, Hq, Hkv, D, rank_call):
     assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("rank_call", ["decode_lse", "prefill"])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_bad_block_on_one_rank_poisons_the_merge(dt, rank_call):
+    """A rank whose table holds an id outside its pool for one sequence (a
+    broken precondition) returns NaN rows and a NaN log-sum-exp for that
+    sequence; the merge must carry the NaN into the merged rows and their
+    log-sum-exp instead of dropping the rank, and leave the other sequences
+    equal to the unsplit oracle."""
+    world, B, Hq, Hkv, D = 2, 16, 8, 2, 64
+    _say(f"cp bad block {dt} via {rank_call}")
+    lens = [17, 40, 100, 257]
+    w = W.custom(lens, Hq, Hkv, D, B, dt, seed=307_357)
+    ref = oracle.run_step(w)["out"]
+    table, nb = _virtual_table(w, world)
+    seq = np.concatenate([w.hist_seq, w.new_seq])
+    pos = np.concatenate([w.hist_pos, w.new_pos])
+    key = np.concatenate([oracle.to_bits(w.hist_key, dt), oracle.to_bits(w.new_key, dt)])
+    val = np.concatenate([oracle.to_bits(w.hist_value, dt), oracle.to_bits(w.new_value, dt)])
+    key_d = _rows(key if dt == "bf16" else key.view(np.float32), dt)
+    val_d = _rows(val if dt == "bf16" else val.view(np.float32), dt)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    bt, cl = dev(table), dev(w.context_lens)
+    q = _rows(w.q, dt)
+    starts = dev(np.arange(w.num_seqs + 1, dtype=np.int32))
+    bad_seq = 2
+    bad_table = table.copy()
+    bad_table[bad_seq, 0] = nb + 5  # rank 1 holds the odd positions of virtual block 0
+    outs, lses = [], []
+    for r in range(world):
+        k, v = pa.empty_kv_cache(nb, Hkv, B, D, tdt, "cuda", fill=float("nan"))
+        pa.write_kv(k, v, key_d, val_d, pa.cp_slot_mapping(bt, dev(seq), dev(pos), B, world, r, 1))
+        local = pa.cp_context_lens(cl, B, world, r, 1)
+        mcl = int(local.max().item())
+        rbt = dev(bad_table) if r == 1 else bt
+        lse = torch.empty((w.num_seqs, Hq), dtype=torch.float32, device="cuda")
+        if rank_call == "prefill":
+            out = pa.prefill(q, k, v, rbt, local, starts, mcl, 1, w.scale, lse=lse)
+        else:
+            out = pa.decode(q, k, v, rbt, local, mcl, w.scale, lse=lse)
+        outs.append(out)
+        lses.append(lse)
+    out_lse = torch.empty((w.num_seqs, Hq), dtype=torch.float32, device="cuda")
+    merged = pa.merge_states(torch.stack(outs), torch.stack(lses), out_lse=out_lse)
+    torch.cuda.synchronize()
+    assert np.isnan(lses[1][bad_seq].cpu().numpy()).all(), "the poisoned rank's lse is not NaN"
+    got, got_lse = as_f64(merged), out_lse.cpu().numpy()
+    assert np.isnan(got[bad_seq]).all() and np.isnan(got_lse[bad_seq]).all()
+    keep = [s for s in range(w.num_seqs) if s != bad_seq]
+    assert np.isfinite(got_lse[keep]).all()
+    assert float(np.max(np.abs(got[keep] - ref[keep]))) <= TOL[dt]
+
+
 @pytest.mark.parametrize("dt,P", [("bf16", 0), ("bf16", 32), ("bf16", 512), ("f32", 0),
                                   ("f32", 64)])
 def test_decode_lse_matches_oracle(dt, P):

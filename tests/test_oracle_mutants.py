@@ -33,6 +33,12 @@ MUTANTS = {
     "gather_misses_last_block": ("for i in range(blocks_needed(L, B)):\n        lo, hi",
                                  "for i in range(max(blocks_needed(L, B) - 1, 1)):\n        lo, hi"),
     "bf16_widen_wrong_shift": ("(bits.astype(np.uint32) << 16)", "(bits.astype(np.uint32) << 15)"),
+    "kv_bytes_counts_k_only": ("return layers * tokens * kv_heads * head_dim * 2 * dtype_size",
+                               "return layers * tokens * kv_heads * head_dim * dtype_size"),
+    "kv_bytes_ignores_layers": ("return layers * tokens * kv_heads * head_dim * 2 * dtype_size",
+                                "return tokens * kv_heads * head_dim * 2 * dtype_size"),
+    "kv_bytes_ignores_dtype": ("return layers * tokens * kv_heads * head_dim * 2 * dtype_size",
+                               "return layers * tokens * kv_heads * head_dim * 2 * 2"),
 }
 
 
