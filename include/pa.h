@@ -26,7 +26,10 @@
  * ---------------------------------------
  * Memory.   Every pointer argument is a device pointer to memory the caller
  *           owns (hipMalloc'ed or a torch tensor's storage).  The library
- *           allocates nothing and keeps no state; calls are thread-safe.
+ *           allocates nothing and keeps no state apart from the fixed scratch
+ *           array of pa_decode_scratch (one per device, part of the loaded
+ *           code); calls are thread-safe except overlapping pa_decode_scratch
+ *           calls on one device.
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  *           stream).  Every call only enqueues work on it and returns; results
  *           are visible after the stream is synchronised.  Device-side faults
@@ -77,7 +80,8 @@ enum {
   PA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required            */
   PA_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed            */
   PA_ERR_NO_BLOCKS = -5,   /* block manager: not enough free blocks (nothing changed) */
-  PA_ERR_STATE = -6        /* block manager: sequence live/idle state does not allow it */
+  PA_ERR_STATE = -6,       /* block manager: sequence live/idle state does not allow it */
+  PA_ERR_TOO_LARGE = -7    /* pa_decode_scratch: the call needs more than its fixed scratch */
 };
 
 enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 };
@@ -346,6 +350,32 @@ int pa_decode_lse(void* out, float* lse, const void* q, const void* k_cache, con
                   int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                   float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                   int32_t dtype, int32_t flags, void* stream);
+
+/*
+ * pa_decode_scratch -- pa_decode with no workspace argument, for callers
+ * that cannot allocate device memory (code being recorded into a HIP graph,
+ * tight serving loops, hosts that forbid hipMalloc): it allocates nothing
+ * itself either.
+ *
+ * Arguments, results and errors as pa_decode without workspace and
+ * workspace_bytes.  With partition_size > 0 the split-KV records go to a
+ * scratch buffer the library holds: a fixed 64 MiB array in device memory,
+ * one per device, present from the library's load until the process ends.
+ * A call whose workspace would exceed it (pa_decode_workspace_bytes with the
+ * same sizes > 64 MiB) returns PA_ERR_TOO_LARGE before anything is enqueued.
+ * The first call on a device also enqueues one kernel that zeroes that
+ * device's buffer.  Every call on a device shares its buffer: calls that
+ * overlap in time on one device (on different streams, or from different
+ * threads without ordering) race and may return wrong results; calls
+ * ordered on one stream do not.  partition_size == 0 runs the single pass,
+ * which needs no buffer.
+ */
+int pa_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, float scale, int32_t partition_size,
+                      int32_t dtype, int32_t flags, void* stream);
 
 /*
  * Context parallelism.

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     decode,
     decode_merge,
     decode_partials,
+    decode_scratch,
     decode_workspace_bytes,
     empty_kv_cache,
     kv_cache_shapes,

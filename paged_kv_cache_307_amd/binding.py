@@ -26,6 +26,7 @@ EXPORTED = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partials", "pa_decode_merge",
     "pa_append_decode", "pa_append_decode_partials", "pa_prefill", "pa_cp_slot_mapping",
     "pa_cp_context_lens", "pa_merge_states", "pa_map_to_kernel_blocks", "pa_decode_lse",
+    "pa_decode_scratch",
 )
 
 
@@ -69,6 +70,8 @@ def load_library():
                          [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, I, F, I, P])
     sig["pa_decode_lse"] = (ctypes.c_int,
                             [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, I, P])
+    sig["pa_decode_scratch"] = (ctypes.c_int,
+                                [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, P])
     sig["pa_cp_slot_mapping"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, I, I, I, P])
     sig["pa_cp_context_lens"] = (ctypes.c_int, [P, P, I, I, I, I, I, P])
     sig["pa_merge_states"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, P])
@@ -258,6 +261,22 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, sca
         s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _ptr(workspace),
         ws_bytes, _dtype_code(q), _flags(shared_blocks), _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def decode_scratch(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                   partition_size=0, out=None, stream=None, shared_blocks=False):
+    """pa_decode with the library's own fixed scratch buffer instead of a
+    workspace (pa_decode_scratch); allocates nothing unless ``out`` is None."""
+    if out is None:
+        out = torch.empty_like(q)
+    dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
+    s, hq, hkv, d, b, nb, mb, mcl = dims
+    st = load_library().pa_decode_scratch(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _dtype_code(q),
+        _flags(shared_blocks), _stream(stream))
+    _check(st, "pa_decode_scratch")
     return out
 
 

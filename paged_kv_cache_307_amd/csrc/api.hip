@@ -217,6 +217,52 @@ int check_append(const void* key, const void* value, int32_t num_seqs) {
   return PA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned scratch for pa_decode_scratch: the split-KV workspace of
+// callers that cannot allocate device memory.  One copy per device, held
+// until the process ends; every pa_decode_scratch call on a device shares
+// it, so calls that overlap on one device race.
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zeroes n16 16-byte words (a fill kernel rather than a memset node, so the
+// first call may be recorded in a graph).
+__global__ void scratch_zero_kernel(uint4* p, int64_t n16) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+constexpr int kMaxScratchDevices = 64;
+
+// The device address of the current device's copy of `scratch`, found once
+// per device with that device current (the array's name is a host-side
+// stand-in, not a device address).  The first call on a device also zeroes
+// the copy on `stream`: the workspace contract wants zeros before the first
+// launch (a stamp of 0 is never used).
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    e = pa::launch(scratch_zero_kernel, dim3(1024), dim3(256), 0, stream,
+                   static_cast<uint4*>(p), int64_t(kScratchBytes / 16));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +276,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_HIP: return "PA_ERR_HIP: HIP launch failed";
     case PA_ERR_NO_BLOCKS: return "PA_ERR_NO_BLOCKS: not enough free KV blocks";
     case PA_ERR_STATE: return "PA_ERR_STATE: sequence is not in the required live/idle state";
+    case PA_ERR_TOO_LARGE:
+      return "PA_ERR_TOO_LARGE: the call needs more than the library's fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -546,6 +594,46 @@ int pa_append_decode(void* out, const void* q, const void* key, const void* valu
   plan.args.new_k = key;
   plan.args.new_v = value;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_partials(plan, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (plan.split) e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);
+  return status_of(e);
+}
+
+int pa_decode_scratch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, float scale, int32_t partition_size,
+                      int32_t dtype, int32_t flags, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (partition_size > 0 && num_seqs > 0 && num_heads > 0 && num_kv_heads > 0 &&
+      head_dim > 0 && num_heads % num_kv_heads == 0 && max_context_len >= 0 &&
+      max_blocks_per_seq >= 0 && block_size > 0) {
+    // the size the split needs, before any launch (the other arguments are
+    // checked by plan_decode below)
+    const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
+    const int64_t need = workspace_bytes_for(num_seqs, num_kv_heads, num_heads / num_kv_heads,
+                                             head_dim, max_parts_for(max_len, partition_size));
+    if (need > int64_t(kScratchBytes)) return PA_ERR_TOO_LARGE;
+    // checks that need no device first, so a bad call touches nothing
+    DecodePlan probe;
+    const int st = plan_decode(&probe, out, q, k_cache, v_cache, block_tables, context_lens,
+                               num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                               num_blocks, max_blocks_per_seq, max_context_len, scale,
+                               partition_size, nullptr, 0, dtype, flags);
+    if (st != PA_OK && st != PA_ERR_WORKSPACE) return st;
+    if (scratch_address(s, &ws) != hipSuccess) return PA_ERR_HIP;
+    ws_bytes = kScratchBytes;
+  }
+  DecodePlan plan;
+  const int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                             num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                             max_blocks_per_seq, max_context_len, scale, partition_size, ws,
+                             ws_bytes, dtype, flags);
+  if (st != PA_OK || plan.args.num_seqs == 0) return st;
   hipError_t e = launch_partials(plan, s);
   if (e != hipSuccess) return PA_ERR_HIP;
   if (plan.split) e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);

@@ -99,6 +99,38 @@ def test_decode_rejects_before_launch(lib, fn, kw, expect):
     assert decode_call(lib, fn, **kw) == expect
 
 
+TOO_LARGE = -7
+
+
+def scratch_call(lib, **kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, S=4, Hq=32, Hkv=8, D=128,
+                B=16, NB=100, MB=64, maxlen=1024, scale=0.088, P=0, dtype=BF16, flags=0)
+    args.update(kw)
+    a = args
+    return lib.pa_decode_scratch(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["S"],
+                                 a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"], a["MB"], a["maxlen"],
+                                 a["scale"], a["P"], a["dtype"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(Hq=30, Hkv=8, P=512), INVALID),
+    (dict(D=96, P=512), UNSUPPORTED),
+    (dict(P=24), INVALID),
+    (dict(P=512, out=None), INVALID),
+    (dict(P=512, q=FAKE_MISALIGNED), INVALID),
+    (dict(P=512, flags=2), INVALID),
+    (dict(S=0, P=512), OK),
+    # a workspace beyond the fixed 64 MiB scratch: 512 sequences of 128K
+    # tokens in 512-token partitions need ~2.2 GB of records
+    (dict(S=512, MB=8192, maxlen=131072, P=512), TOO_LARGE),
+    # 6000 sequences of 1024 tokens: 8 KV heads x 5 records x 2096 bytes each
+    (dict(S=6000, MB=64, maxlen=1024, P=1024), TOO_LARGE),
+])
+def test_decode_scratch_rejects_before_launch(lib, kw, expect):
+    assert scratch_call(lib, **kw) == expect
+    assert "TOO_LARGE" in pa.status_string(TOO_LARGE)
+
+
 def test_merge_rejects_before_launch(lib):
     m = lib.pa_decode_merge
     assert m(FAKE, FAKE, 4, 30, 8, 128, 64, 16, 1024, 512, FAKE, 1 << 30, BF16, None) == INVALID
