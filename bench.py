@@ -11,10 +11,13 @@ With --separate-write the rows go through pa_write_kv first and the decode
 is pa_decode_partials + pa_decode_merge.  The partition size defaults to one at least as long as the
 workload's longest context (so records only arise where a worker's slice
 cuts a pair); the long-context workload keeps its 512-token partitions.
-When the workload's block tables share blocks between sequences (the
-shared-prefix workloads) the decode gets PA_DECODE_SHARED_BLOCKS, so shared
-blocks stay cacheable; otherwise K/V tiles are streamed (``--shared-blocks``
-overrides the choice).
+The shared-prefix workloads decode with pa_decode_shared_prefix (rows
+appended), told which sequences share their prefix blocks, so each shared
+block is streamed once per KV head; ``--no-groups`` decodes them as any other
+batch instead, with PA_DECODE_SHARED_BLOCKS so that the shared blocks stay
+cacheable.  Otherwise K/V tiles are streamed (``--shared-blocks`` overrides
+the choice).  Bytes: a slot read by several sequences counts once
+(``value``, roofline); ``logical_*`` fields count every sequence's reads.
 
 The default workload is the Llama-3-8B-shaped decode layer: 64 sequences,
 32 query / 8 KV heads, head_dim 128, bf16, B=16, context lengths uniform on
@@ -56,7 +59,7 @@ KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
 MEASURED_TRAFFIC = {
-    ("llama3_8b_decode", 4096, True, False): {
+    ("llama3_8b_decode", 4096, True, False, False): {
         "bytes": 553867967, "fetch_bytes": 549001823, "write_bytes": 4866144,
         "sources_sha256": "6f946f039748493493f0909c691cea37e47ddb3517aa81b8a2104a1b97bee7fe"},
 }
@@ -163,10 +166,10 @@ def shares_blocks(w):
     return len(np.unique(ids)) < len(ids)
 
 
-def measured_traffic(workload, partition, append, shared):
+def measured_traffic(workload, partition, append, shared, groups=False):
     """Counter-derived HBM bytes per launch, or None when there is no
     measurement for this workload and step or the kernel changed since."""
-    rec = MEASURED_TRAFFIC.get((workload, partition, append, shared))
+    rec = MEASURED_TRAFFIC.get((workload, partition, append, shared, groups))
     if rec is None or rec["sources_sha256"] != kernel_sources_sha256():
         return None
     return rec["bytes"]
@@ -637,7 +640,12 @@ def main():
     ap.add_argument("--separate-write", action="store_true",
                     help="write the step's rows with pa_write_kv, then pa_decode_partials")
     ap.add_argument("--shared-blocks", choices=["auto", "on", "off"], default="auto",
-                    help="PA_DECODE_SHARED_BLOCKS: auto = when the tables share blocks")
+                    help="PA_DECODE_SHARED_BLOCKS: auto = when the tables share blocks and "
+                         "the decode is not told the groups")
+    ap.add_argument("--no-groups", action="store_true",
+                    help="shared-prefix workloads: decode with pa_append_decode_partials "
+                         "(every sequence reads its shared blocks) instead of "
+                         "pa_decode_shared_prefix")
     ap.add_argument("--cp-world", type=int, default=0,
                     help="context-parallel ranks to emulate on the decode layer (0 = off)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -675,7 +683,11 @@ def main():
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     B = w.block_size
     P = default_partition if args.partition is None else args.partition
-    shared = shares_blocks(w) if args.shared_blocks == "auto" else args.shared_blocks == "on"
+    # shared-prefix workloads: the decode is told which sequences share their
+    # prefix blocks (each such block is then streamed once per KV head)
+    groups = "prefix_len" in w.extra and not args.no_groups and not args.separate_write
+    shared = (shares_blocks(w) and not groups) if args.shared_blocks == "auto" \
+        else args.shared_blocks == "on"
     # some pair spans more than one partition (selects the kernel variant)
     multi_part = -(-min(w.max_context_len, w.max_blocks_per_seq * B) // P) > 1
     hist_bt, bt, cl = t(w.hist_block_tables), t(w.block_tables), t(w.context_lens)
@@ -694,12 +706,22 @@ def main():
     # private block first; repeating the copy every step restores the same
     # state (the sources never change, and each branch then rewrites its slot)
     copies = t(w.copy_pairs) if len(w.copy_pairs) else None
-    ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, P, dev)
+    if groups:
+        ng, br = w.extra["num_groups"], w.extra["branches"]
+        gs = torch.arange(0, ng * br + 1, br, dtype=torch.int32, device=dev)
+        pl = torch.full((ng,), w.extra["prefix_len"], dtype=torch.int32, device=dev)
+        ws = pa.alloc_shared_prefix_workspace(w.num_seqs, w.num_heads, w.num_kv_heads,
+                                              w.head_dim, mcl, P, ng, dev)
+    else:
+        ws = pa.alloc_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, mcl, P, dev)
     torch.cuda.synchronize()
 
     def partials(i):
         k, v = layers[i % len(layers)]
-        if args.separate_write:
+        if groups:
+            pa.decode_shared_prefix(q, k, v, bt, cl, gs, pl, mcl, w.scale, P, ws, out, key=new_k,
+                                    value=new_v, shared_blocks=shared, partials_only=True)
+        elif args.separate_write:
             pa.decode_partials(q, k, v, bt, cl, mcl, w.scale, P, ws, out, shared_blocks=shared)
         else:
             pa.append_decode_partials(q, new_k, new_v, k, v, bt, cl, mcl, w.scale, P, ws, out,
@@ -712,7 +734,11 @@ def main():
         if args.separate_write:
             pa.write_kv(k, v, new_k, new_v, new_slots)
         partials(i)
-        pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
+        if groups:
+            pa.decode_shared_prefix_merge(out, cl, gs, pl, w.num_kv_heads, B,
+                                          w.max_blocks_per_seq, mcl, P, ws)
+        else:
+            pa.decode_merge(out, cl, w.num_kv_heads, B, w.max_blocks_per_seq, mcl, P, ws)
 
     for i in range(args.warmup):
         step(i)
@@ -801,8 +827,12 @@ def main():
             "partition_size": P, "layers_rotated": args.layers,
             "kv_loads": "cached (PA_DECODE_SHARED_BLOCKS)" if shared else "streamed (nontemporal)",
             "step": (("pa_copy_blocks + " if copies is not None else "") +
-                     ("pa_write_kv + pa_decode_partials + pa_decode_merge" if args.separate_write
+                     ("pa_decode_shared_prefix_partials (rows appended) + "
+                      "pa_decode_shared_prefix_merge" if groups else
+                      "pa_write_kv + pa_decode_partials + pa_decode_merge" if args.separate_write
                       else "pa_append_decode_partials + pa_decode_merge")),
+            "prefix_groups": ({"groups": w.extra["num_groups"], "members": w.extra["branches"],
+                               "shared_tokens": w.extra["prefix_len"]} if groups else None),
             "copy_pairs": len(w.copy_pairs),
         },
         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -814,14 +844,16 @@ def main():
         "capacity": capacity_figures(w),
         "roofline": {
             "kernel": f"decode_bf16_mfma_kernel<{w.head_dim},{B},true,{str(not shared).lower()},"
-                      f"{str(multi_part).lower()}> (" +
-                      ("pa_decode_partials" if args.separate_write else "pa_append_decode_partials") + ")",
+                      f"{str(multi_part or groups).lower()},{str(groups).lower()}> (" +
+                      ("pa_decode_shared_prefix_partials" if groups else
+                       "pa_decode_partials" if args.separate_write else
+                       "pa_append_decode_partials") + ")",
             "bound": "hbm", "achieved": round(part_gbs, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(part_gbs / HBM_PEAK_GBS, 4),
             "avg_us": round(part_avg_ms * 1e3, 3), "per_launch_us": launch_pct,
             "bytes_per_launch": part_bytes,
             "logical_bytes_per_launch": kernel_bytes(ab_logical),
-            "traffic": measured_traffic(w.name, P, not args.separate_write, shared),
+            "traffic": measured_traffic(w.name, P, not args.separate_write, shared, groups),
             "traffic_source": "rocprofv3 FETCH_SIZE and WRITE_SIZE passes of this workload's "
                               "step, recorded for the current kernel sources (null once they "
                               "change)",

@@ -352,6 +352,85 @@ int pa_decode_lse(void* out, float* lse, const void* q, const void* k_cache, con
                   int32_t dtype, int32_t flags, void* stream);
 
 /*
+ * Shared-prefix decode.
+ * [P1 共享但不污染状态: branches sampled from one prompt reference the same
+ *  physical blocks for their common tokens (reference counted, immutable)
+ *  until a branch writes into a shared block, which copy-on-write first
+ *  makes private; P2 section 2.1 (共享与写时复制): physical blocks are shared
+ *  across sequences through their block tables.]
+ *
+ * pa_decode_shared_prefix computes exactly what pa_decode (with key/value:
+ * pa_append_decode) computes, and is told which sequences share blocks so
+ * that each shared block is read once per KV head for all the sharers'
+ * query heads instead of once per sequence:
+ *
+ *   group_start  in  int32 [num_groups + 1], device: group i is sequences
+ *                    group_start[i] .. group_start[i+1] - 1 (consecutive in
+ *                    the batch; groups in increasing order, disjoint)
+ *   prefix_lens  in  int32 [num_groups], device: the first prefix_lens[i]
+ *                    tokens of every member of group i lie in the same
+ *                    physical blocks (the members' tables agree on those
+ *                    entries)
+ *   key, value   in  as pa_append_decode, or both NULL (no row appended)
+ *   other arguments as pa_decode; partition_size must be > 0, and the
+ *   workspace at least pa_decode_shared_prefix_workspace_bytes(...) long
+ *   (16-byte aligned, zero-filled once, reusable as pa_decode's).
+ *
+ * Each group's shared tokens, rounded down to a multiple of 16 and to the
+ * first member's length, are streamed once per KV head through the first
+ * member's table, with the query heads of up to 64 / G members (32 / G at
+ * head_dim 256) as matrix-core columns; the members' other tokens are
+ * decoded as pa_decode does, and a log-sum-exp merge combines the two.
+ * Members beyond that count decode all their tokens themselves, so any
+ * group size is correct.  Preconditions: the tables agree as stated (the
+ * shared tokens are read through the first member's table), and with
+ * key/value a member's row position L - 1 lies past its shared tokens
+ * (copy-on-write has made the block it is written into private); a row
+ * whose position lies inside them is not written.  Broken preconditions
+ * give wrong values, never out-of-bounds accesses.  The fp32 kernel ignores
+ * the groups (it decodes every sequence's tokens; same results).
+ * pa_decode_shared_prefix_partials and pa_decode_shared_prefix_merge are
+ * its two launches, callable one by one.  Errors as pa_decode, plus
+ * PA_ERR_INVALID_ARG for num_groups < 0, partition_size <= 0, NULL group
+ * arrays (num_groups > 0), or only one of key / value, and
+ * PA_ERR_UNSUPPORTED for num_groups > 512.
+ */
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t partition_size,
+                                               int32_t num_groups);
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* key, const void* value,
+                            void* k_cache, void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* group_start,
+                            const int32_t* prefix_lens, int32_t num_groups, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, int32_t dtype,
+                            int32_t flags, void* stream);
+
+int pa_decode_shared_prefix_partials(void* out, const void* q, const void* key, const void* value,
+                                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* group_start,
+                                     const int32_t* prefix_lens, int32_t num_groups,
+                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, int32_t dtype, int32_t flags,
+                                     void* stream);
+
+int pa_decode_shared_prefix_merge(void* out, const int32_t* context_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int32_t num_groups, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t block_size,
+                                  int32_t max_context_len, int32_t partition_size,
+                                  const void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream);
+
+/*
  * pa_decode_scratch -- pa_decode with no workspace argument, for callers
  * that cannot allocate device memory (code being recorded into a HIP graph,
  * tight serving loops, hosts that forbid hipMalloc): it allocates nothing

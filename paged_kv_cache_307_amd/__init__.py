@@ -18,6 +18,10 @@ from .binding import (  # noqa: F401
     decode_merge,
     decode_partials,
     decode_scratch,
+    decode_shared_prefix,
+    decode_shared_prefix_merge,
+    decode_shared_prefix_workspace_bytes,
+    alloc_shared_prefix_workspace,
     decode_workspace_bytes,
     empty_kv_cache,
     kv_cache_shapes,

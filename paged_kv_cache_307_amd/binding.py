@@ -26,7 +26,8 @@ EXPORTED = (
     "pa_decode_workspace_bytes", "pa_decode", "pa_decode_partials", "pa_decode_merge",
     "pa_append_decode", "pa_append_decode_partials", "pa_prefill", "pa_cp_slot_mapping",
     "pa_cp_context_lens", "pa_merge_states", "pa_map_to_kernel_blocks", "pa_decode_lse",
-    "pa_decode_scratch",
+    "pa_decode_scratch", "pa_decode_shared_prefix_workspace_bytes", "pa_decode_shared_prefix",
+    "pa_decode_shared_prefix_partials", "pa_decode_shared_prefix_merge",
 )
 
 
@@ -72,6 +73,12 @@ def load_library():
                             [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, Z, I, I, P])
     sig["pa_decode_scratch"] = (ctypes.c_int,
                                 [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, I, I, P])
+    sig["pa_decode_shared_prefix_workspace_bytes"] = (Z, [I, I, I, I, I, I, I])
+    for name in ("pa_decode_shared_prefix", "pa_decode_shared_prefix_partials"):
+        sig[name] = (ctypes.c_int, [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I,
+                                    P, Z, I, I, P])
+    sig["pa_decode_shared_prefix_merge"] = (ctypes.c_int,
+                                            [P, P, P, P, I, I, I, I, I, I, I, I, I, P, Z, I, P])
     sig["pa_cp_slot_mapping"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, I, I, I, P])
     sig["pa_cp_context_lens"] = (ctypes.c_int, [P, P, I, I, I, I, I, P])
     sig["pa_merge_states"] = (ctypes.c_int, [P, P, P, P, I, I, I, I, P])
@@ -261,6 +268,76 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, sca
         s, hq, hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _ptr(workspace),
         ws_bytes, _dtype_code(q), _flags(shared_blocks), _stream(stream))
     _check(st, "pa_decode")
+    return out
+
+
+def decode_shared_prefix_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                         max_context_len, partition_size, num_groups):
+    return int(load_library().pa_decode_shared_prefix_workspace_bytes(
+        num_seqs, num_heads, num_kv_heads, head_dim, int(max_context_len), int(partition_size),
+        int(num_groups)))
+
+
+def alloc_shared_prefix_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                  partition_size, num_groups, device="cuda"):
+    n = decode_shared_prefix_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                             max_context_len, partition_size, num_groups)
+    return torch.zeros(max(n, 16) // 4 + 4, dtype=torch.float32, device=device)
+
+
+def _group_args(group_start, prefix_lens):
+    _cuda_contig("group_start", group_start, torch.int32)
+    _cuda_contig("prefix_lens", prefix_lens, torch.int32)
+    g = prefix_lens.numel()
+    _need(group_start.numel() == g + 1, "group_start must be [num_groups + 1]")
+    return g
+
+
+def decode_shared_prefix(q, k_cache, v_cache, block_tables, context_lens, group_start,
+                         prefix_lens, max_context_len, scale, partition_size, workspace=None,
+                         out=None, key=None, value=None, stream=None, shared_blocks=True,
+                         partials_only=False):
+    """pa_decode_shared_prefix: pa_decode (with key/value: pa_append_decode)
+    told that sequences group_start[i] .. group_start[i+1]-1 share the
+    blocks of their first prefix_lens[i] tokens.  partials_only: the first
+    launch alone (pa_decode_shared_prefix_partials)."""
+    if out is None:
+        out = torch.empty_like(q)
+    dims = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len)
+    s, hq, hkv, d, b, nb, mb, mcl = dims
+    g = _group_args(group_start, prefix_lens)
+    if workspace is None:
+        workspace = alloc_shared_prefix_workspace(s, hq, hkv, d, mcl, partition_size, g,
+                                                  device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _need((key is None) == (value is None), "give both key and value, or neither")
+    if key is not None:
+        for name, t in (("key", key), ("value", value)):
+            _cuda_contig(name, t, k_cache.dtype)
+            _need(tuple(t.shape) == (s, hkv, d), f"{name} must be [S, Hkv, D]")
+    fn = "pa_decode_shared_prefix_partials" if partials_only else "pa_decode_shared_prefix"
+    st = getattr(load_library(), fn)(
+        _ptr(out), _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_tables), _ptr(context_lens), _ptr(group_start), _ptr(prefix_lens), g, s, hq,
+        hkv, d, b, nb, mb, mcl, float(scale), int(partition_size), _ptr(workspace), ws_bytes,
+        _dtype_code(q), _flags(shared_blocks), _stream(stream))
+    _check(st, fn)
+    return out
+
+
+def decode_shared_prefix_merge(out, context_lens, group_start, prefix_lens, num_kv_heads,
+                               block_size, max_blocks_per_seq, max_context_len, partition_size,
+                               workspace, stream=None):
+    _cuda_contig("out", out)
+    _cuda_contig("context_lens", context_lens, torch.int32)
+    s, hq, d = out.shape
+    g = _group_args(group_start, prefix_lens)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().pa_decode_shared_prefix_merge(
+        _ptr(out), _ptr(context_lens), _ptr(group_start), _ptr(prefix_lens), g, s, hq,
+        num_kv_heads, d, max_blocks_per_seq, block_size, int(max_context_len),
+        int(partition_size), _ptr(workspace), ws_bytes, _dtype_code(out), _stream(stream))
+    _check(st, "pa_decode_shared_prefix_merge")
     return out
 
 

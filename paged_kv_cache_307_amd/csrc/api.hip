@@ -113,9 +113,52 @@ uint32_t next_epoch() {
   return e == 0 ? 1u : e;
 }
 
-int decode_workers(bool bf16, int head_dim, int block_size) {
-  return bf16 ? pa::decode_workers_bf16_mfma(head_dim, block_size)
+int decode_workers(bool bf16, int head_dim, int block_size, bool groups = false) {
+  return bf16 ? pa::decode_workers_bf16_mfma(head_dim, block_size, groups)
               : pa::decode_workers_simt(head_dim, false);
+}
+
+// Line weights of a grouped launch (schedule.h), in quarter tiles of
+// streaming time, fitted to per-worker timelines of the shared-prefix batch
+// on MI355X: a tail tile 4; a prefix tile (which also feeds 64 query
+// columns) 6; a tail run's start (table window, queries, then the first
+// tile: two dependent memory round trips) 23; a prefix run's start and end
+// (queries of 64 columns, and one record per member stored) 52.
+constexpr int kTailWt = 4;
+constexpr int kTailLead = 23;
+constexpr int kPrefixWt = 6;
+constexpr int kPrefixLead = 52;
+
+void set_group_weights(DecodeArgs& a) {
+  a.tail_lead = kTailLead;
+  a.tail_wt = kTailWt;
+  a.prefix_lead = kPrefixLead;
+  a.prefix_wt = kPrefixWt;
+}
+
+// Longest context the split-schedule size check should assume for a grouped
+// line: a pair's positions are its tiles times the heavier weight plus a lead.
+int64_t weighted_len(int64_t max_len) {
+  const int wt = kPrefixWt > kTailWt ? kPrefixWt : kTailWt;
+  const int lead = kTailLead > kPrefixLead ? kTailLead : kPrefixLead;
+  return max_len * wt + 16 * int64_t(lead);
+}
+
+// Query columns of a prefix unit (bf16 kernel): 64 at head_dim <= 128, 32
+// at 256; the members a unit serves are those columns / group size.
+int prefix_members_for(int32_t head_dim, int32_t group) {
+  return (head_dim <= 128 ? 64 : 32) / group;
+}
+
+// Workspace of a grouped (shared-prefix) launch: the meta block over
+// num_groups + S units, the tail records (as a plain launch's), then the
+// wide records of the prefix pieces.
+int64_t group_workspace_bytes_for(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
+                                  int32_t head_dim, int64_t max_parts, int32_t num_groups) {
+  const int64_t rec = pa::record_floats(group, head_dim) * int64_t(sizeof(float));
+  return pa::meta_bytes_units(num_seqs + num_groups) +
+         pa::max_records(num_seqs, num_kv_heads, max_parts) * rec +
+         pa::max_wide_records(num_groups, num_kv_heads) * prefix_members_for(head_dim, group) * rec;
 }
 
 // Validate the decode arguments and fill the launch plan.  Returns PA_OK with
@@ -125,7 +168,14 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                 int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                size_t workspace_bytes, int32_t dtype, int32_t flags) {
+                size_t workspace_bytes, int32_t dtype, int32_t flags,
+                const int32_t* group_start = nullptr, const int32_t* prefix_lens = nullptr,
+                int32_t num_groups = 0) {
+  if (num_groups < 0) return PA_ERR_INVALID_ARG;
+  if (num_groups > pa::kMaxGroups) return PA_ERR_UNSUPPORTED;
+  if (num_groups > 0 && partition_size <= 0) return PA_ERR_INVALID_ARG;  // grouped: split only
+  if (num_groups > 0 && num_seqs > 0 && (!group_start || !prefix_lens)) return PA_ERR_INVALID_ARG;
+  if (int64_t(num_seqs) + num_groups > 0x3FFFFFFF) return PA_ERR_UNSUPPORTED;
   if ((flags & ~int32_t(PA_DECODE_SHARED_BLOCKS)) != 0) return PA_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_blocks < 0 ||
       max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
@@ -148,21 +198,41 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
   if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
 
   const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
-  // the split schedule sums 16-token tiles over sequences in 32-bit integers
-  // and divides line positions (tiles x KV heads) times workers in doubles
-  if (partition_size > 0 && !split_line_fits(num_seqs, num_kv_heads, max_len))
+  // the split schedule sums 16-token tiles over sequences (and prefix units)
+  // in 32-bit integers and divides line positions (tiles x KV heads) times
+  // workers in doubles
+  if (partition_size > 0 &&
+      !split_line_fits(num_seqs + num_groups, num_kv_heads,
+                       num_groups > 0 ? weighted_len(max_len) : max_len))
     return PA_ERR_UNSUPPORTED;
   DecodeArgs& a = plan->args;
   plan->split = partition_size > 0;
   if (plan->split) {
     const int64_t parts = max_parts_for(max_len, partition_size);
-    const int64_t need = workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts);
+    // the fp32 kernel has no prefix units: it decodes every token of every
+    // sequence (the same result), in a plain layout that fits the grouped one
+    const bool groups = num_groups > 0 && dtype == PA_DTYPE_BF16;
+    const int64_t need =
+        num_groups > 0
+            ? group_workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts, num_groups)
+            : workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts);
     if (!workspace || int64_t(workspace_bytes) < need || !aligned16(workspace))
       return PA_ERR_WORKSPACE;
-    const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size);
+    const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size, groups);
     if (workers <= 0) return PA_ERR_HIP;
     a.ws_meta = workspace;
-    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + pa::meta_bytes(num_seqs));
+    a.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    (groups ? pa::meta_bytes_units(num_seqs + num_groups)
+                                            : pa::meta_bytes(num_seqs)));
+    if (groups) {
+      a.ws_wide = a.ws + pa::max_records(num_seqs, num_kv_heads, parts) *
+                             pa::record_floats(group, head_dim);
+      a.group_start = group_start;
+      a.prefix_lens = prefix_lens;
+      a.num_groups = num_groups;
+      a.prefix_members = prefix_members_for(head_dim, group);
+      set_group_weights(a);
+    }
     a.workers = workers;
     a.partition_size = partition_size;
     a.max_partitions = int32_t(parts);
@@ -215,6 +285,112 @@ int check_append(const void* key, const void* value, int32_t num_seqs) {
   if (!key || !value) return PA_ERR_INVALID_ARG;
   if (!aligned16(key) || !aligned16(value)) return PA_ERR_INVALID_ARG;
   return PA_OK;
+}
+
+// The merge launch of a split decode (plain, or grouped with num_groups > 0),
+// rebuilt from its sizes: the same schedule and workspace layout as the
+// partials launch.
+int merge_call(void* out, const int32_t* context_lens, const int32_t* group_start,
+               const int32_t* prefix_lens, int32_t num_groups, int32_t num_seqs,
+               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+               int32_t max_blocks_per_seq, int32_t block_size, int32_t max_context_len,
+               int32_t partition_size, const void* workspace, size_t workspace_bytes,
+               int32_t dtype, void* stream) {
+  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 0 ||
+      max_context_len < 0 || partition_size < 0 || num_heads % num_kv_heads != 0 ||
+      num_groups < 0)
+    return PA_ERR_INVALID_ARG;
+  if (elem_bytes_of(dtype) == 0) return PA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
+  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
+  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
+    return PA_ERR_INVALID_ARG;
+  if (num_groups > 0 && partition_size == 0) return PA_ERR_INVALID_ARG;
+  if (num_groups > pa::kMaxGroups) return PA_ERR_UNSUPPORTED;
+  if (int64_t(num_seqs) + num_groups > 0x3FFFFFFF) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || partition_size == 0) return PA_OK;
+  if (!out || !context_lens) return PA_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!group_start || !prefix_lens)) return PA_ERR_INVALID_ARG;
+  if (!aligned16(out)) return PA_ERR_INVALID_ARG;
+  const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
+  const int64_t parts = max_parts_for(max_len, partition_size);
+  const int32_t group = num_heads / num_kv_heads;
+  const int64_t need =
+      num_groups > 0
+          ? group_workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts, num_groups)
+          : workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts);
+  if (!workspace || !aligned16(workspace) || int64_t(workspace_bytes) < need)
+    return PA_ERR_WORKSPACE;
+  if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
+  if (!split_line_fits(num_seqs + num_groups, num_kv_heads,
+                       num_groups > 0 ? weighted_len(max_len) : max_len))
+    return PA_ERR_UNSUPPORTED;
+  const bool bf16 = dtype == PA_DTYPE_BF16;
+  const bool groups = num_groups > 0 && bf16;
+  const int workers = decode_workers(bf16, head_dim, block_size, groups);
+  if (workers <= 0) return PA_ERR_HIP;
+  DecodeArgs a{};
+  char* ws = static_cast<char*>(const_cast<void*>(workspace));
+  a.out = out;
+  a.context_lens = context_lens;
+  a.ws_meta = ws;
+  a.ws = reinterpret_cast<float*>(ws + (groups ? pa::meta_bytes_units(num_seqs + num_groups)
+                                               : pa::meta_bytes(num_seqs)));
+  if (groups) {
+    a.ws_wide = a.ws + pa::max_records(num_seqs, num_kv_heads, parts) *
+                           pa::record_floats(group, head_dim);
+    a.group_start = group_start;
+    a.prefix_lens = prefix_lens;
+    a.num_groups = num_groups;
+    a.prefix_members = prefix_members_for(head_dim, group);
+    set_group_weights(a);
+  }
+  a.workers = workers;
+  a.split = 1;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = group;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = int32_t(max_len);
+  a.partition_size = partition_size;
+  a.max_partitions = int32_t(parts);
+  return status_of(pa::launch_decode_merge(a, head_dim, block_size, bf16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+// A grouped decode: partials (with the step's rows appended when key and
+// value are given), then the merge unless partials_only.
+int shared_prefix_call(void* out, const void* q, const void* key, const void* value,
+                       void* k_cache, void* v_cache, const int32_t* block_tables,
+                       const int32_t* context_lens, const int32_t* group_start,
+                       const int32_t* prefix_lens, int32_t num_groups, int32_t num_seqs,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_context_len, float scale, int32_t partition_size,
+                       void* workspace, size_t workspace_bytes, int32_t dtype, int32_t flags,
+                       void* stream, bool partials_only) {
+  if ((key == nullptr) != (value == nullptr)) return PA_ERR_INVALID_ARG;
+  if (partition_size <= 0) return PA_ERR_INVALID_ARG;
+  DecodePlan plan;
+  int st = plan_decode(&plan, out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, dtype, flags, group_start, prefix_lens, num_groups);
+  if (st != PA_OK) return st;
+  if (key) {
+    st = check_append(key, value, num_seqs);
+    if (st != PA_OK) return st;
+  }
+  if (plan.args.num_seqs == 0) return PA_OK;
+  plan.args.new_k = key;
+  plan.args.new_v = value;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_partials(plan, s);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  if (!partials_only)
+    e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);
+  return status_of(e);
 }
 
 // ---------------------------------------------------------------------------
@@ -358,45 +534,9 @@ int pa_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs, in
                     int32_t num_kv_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                     int32_t block_size, int32_t max_context_len, int32_t partition_size,
                     const void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
-  if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || max_blocks_per_seq < 0 ||
-      max_context_len < 0 || partition_size < 0 || num_heads % num_kv_heads != 0)
-    return PA_ERR_INVALID_ARG;
-  if (elem_bytes_of(dtype) == 0) return PA_ERR_UNSUPPORTED;
-  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return PA_ERR_UNSUPPORTED;
-  if (num_heads / num_kv_heads > 16) return PA_ERR_UNSUPPORTED;
-  if (partition_size > 0 && (partition_size % 16 != 0 || partition_size % block_size != 0))
-    return PA_ERR_INVALID_ARG;
-  if (num_seqs == 0 || partition_size == 0) return PA_OK;
-  if (!out || !context_lens) return PA_ERR_INVALID_ARG;
-  if (!aligned16(out)) return PA_ERR_INVALID_ARG;
-  const int64_t max_len = effective_max_len(max_context_len, max_blocks_per_seq, block_size);
-  const int64_t parts = max_parts_for(max_len, partition_size);
-  const int32_t group = num_heads / num_kv_heads;
-  if (!workspace || !aligned16(workspace) ||
-      int64_t(workspace_bytes) < workspace_bytes_for(num_seqs, num_kv_heads, group, head_dim, parts))
-    return PA_ERR_WORKSPACE;
-  if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-  if (!split_line_fits(num_seqs, num_kv_heads, max_len)) return PA_ERR_UNSUPPORTED;
-  const int workers = decode_workers(dtype == PA_DTYPE_BF16, head_dim, block_size);
-  if (workers <= 0) return PA_ERR_HIP;
-  DecodeArgs a{};
-  a.out = out;
-  a.context_lens = context_lens;
-  a.ws_meta = const_cast<void*>(workspace);
-  a.ws = reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) +
-                                  pa::meta_bytes(num_seqs));
-  a.workers = workers;
-  a.split = 1;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.group = group;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_context_len = int32_t(max_len);
-  a.partition_size = partition_size;
-  a.max_partitions = int32_t(parts);
-  return status_of(pa::launch_decode_merge(a, head_dim, block_size, dtype == PA_DTYPE_BF16,
-                                           static_cast<hipStream_t>(stream)));
+  return merge_call(out, context_lens, nullptr, nullptr, 0, num_seqs, num_heads, num_kv_heads,
+                    head_dim, max_blocks_per_seq, block_size, max_context_len, partition_size,
+                    workspace, workspace_bytes, dtype, stream);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -638,6 +778,67 @@ int pa_decode_scratch(void* out, const void* q, const void* k_cache, const void*
   if (e != hipSuccess) return PA_ERR_HIP;
   if (plan.split) e = pa::launch_decode_merge(plan.args, plan.head_dim, plan.block_size, plan.bf16, s);
   return status_of(e);
+}
+
+size_t pa_decode_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t max_context_len, int32_t partition_size,
+                                               int32_t num_groups) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || partition_size <= 0 || num_groups < 0 ||
+      num_groups > pa::kMaxGroups ||
+      num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16)
+    return 0;
+  const int64_t parts = max_parts_for(max_context_len, partition_size);
+  return size_t(group_workspace_bytes_for(num_seqs, num_kv_heads, num_heads / num_kv_heads,
+                                          head_dim, parts, num_groups));
+}
+
+int pa_decode_shared_prefix(void* out, const void* q, const void* key, const void* value,
+                            void* k_cache, void* v_cache, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* group_start,
+                            const int32_t* prefix_lens, int32_t num_groups, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                            int32_t max_context_len, float scale, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes, int32_t dtype,
+                            int32_t flags, void* stream) {
+  return shared_prefix_call(out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                            group_start, prefix_lens, num_groups, num_seqs, num_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                            max_context_len, scale, partition_size, workspace, workspace_bytes,
+                            dtype, flags, stream, false);
+}
+
+int pa_decode_shared_prefix_partials(void* out, const void* q, const void* key, const void* value,
+                                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     const int32_t* context_lens, const int32_t* group_start,
+                                     const int32_t* prefix_lens, int32_t num_groups,
+                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t max_blocks_per_seq, int32_t max_context_len,
+                                     float scale, int32_t partition_size, void* workspace,
+                                     size_t workspace_bytes, int32_t dtype, int32_t flags,
+                                     void* stream) {
+  return shared_prefix_call(out, q, key, value, k_cache, v_cache, block_tables, context_lens,
+                            group_start, prefix_lens, num_groups, num_seqs, num_heads,
+                            num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                            max_context_len, scale, partition_size, workspace, workspace_bytes,
+                            dtype, flags, stream, true);
+}
+
+int pa_decode_shared_prefix_merge(void* out, const int32_t* context_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int32_t num_groups, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_blocks_per_seq, int32_t block_size,
+                                  int32_t max_context_len, int32_t partition_size,
+                                  const void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  void* stream) {
+  if (partition_size <= 0) return PA_ERR_INVALID_ARG;
+  return merge_call(out, context_lens, group_start, prefix_lens, num_groups, num_seqs, num_heads,
+                    num_kv_heads, head_dim, max_blocks_per_seq, block_size, max_context_len,
+                    partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
 }  // extern "C"

@@ -74,8 +74,9 @@ __device__ __forceinline__ void fold_into(Fold<CPL>& a, const Fold<CPL>& b) {
 }
 
 // NW waves per (sequence, query head): one wave for pairs with few records,
-// more when partitions are many.
-template <typename Elem, int D, int NW>
+// more when partitions are many.  kGroups: a grouped launch (shared-prefix
+// groups, schedule.h): a member also folds its prefix pair's records.
+template <typename Elem, int D, int NW, bool kGroups>
 __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int B) {
   constexpr int CH = D / 4 < kThreads ? D / 4 : kThreads;  // float4 chunks per lane group
   constexpr int CPL = D / 4 / CH;                          // chunks per lane (1 up to D = 256)
@@ -152,12 +153,50 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
   asm volatile("" ::: "memory");
 
   PairRecords pr;
-  if (!pair_records(a, B, s, kvh, &pr)) {  // empty sequence
+  UnitRecords ur;
+  bool empty;
+  if constexpr (kGroups) {
+    unit_records(a, B, s, kvh, &ur);
+    pr = ur.tail;
+    empty = ur.len == 0;
+  } else {
+    empty = !pair_records(a, B, s, kvh, &pr);
+  }
+  if (empty) {  // empty sequence
     for (int i = lane + wave * kThreads; i < D; i += kThreads * NW) out[i] = from_f32<Elem>(0.f);
     if (a.lse && threadIdx.x == 0) a.lse[int64_t(s) * a.num_heads + h] = -INFINITY;
     return;
   }
   if (pr.whole) return;  // written whole by its worker
+  if constexpr (kGroups) {
+    // the prefix pieces: one wide slot per worker that streamed part of the
+    // group's shared tokens for this KV head, this member's record in it.
+    // A member shorter than a piece's tokens has l = 0 there: skipped.
+    // The loads of kWideUnroll records per lane go out together (clamped to
+    // the last piece), so a member costs one more round trip to memory.
+    if (ur.prefix) {
+      constexpr int kWideUnroll = 4;
+      const int64_t mslot = int64_t(ur.member);
+      for (int k0 = pg; k0 < ur.wide_count; k0 += PG * kWideUnroll) {
+        Loaded r[kWideUnroll];
+#pragma unroll
+        for (int u = 0; u < kWideUnroll; ++u) {
+          const int64_t k = min(k0 + u * PG, ur.wide_count - 1);
+          const float* rec = a.ws_wide + ((ur.wide + k) * a.prefix_members + mslot) * R;
+          r[u].st = __float_as_uint(rec[G * D + 2 * G]);
+          r[u].m = rec[G * D + hl];
+          r[u].l = rec[G * D + G + hl];
+#pragma unroll
+          for (int i = 0; i < CPL; ++i)
+            r[u].o[i] = *reinterpret_cast<const float4*>(rec + hl * D + 4 * (c + CH * i));
+        }
+#pragma unroll
+        for (int u = 0; u < kWideUnroll; ++u)
+          if (k0 + u * PG < ur.wide_count && r[u].st == pr.epoch && !(r[u].l == 0.f))
+            fold_record(r[u].m, r[u].l, r[u].o);
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < KF; ++u) {
     const int k = pg + u * PG;
@@ -223,14 +262,24 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
 constexpr int kWideMergeParts = 8;
 constexpr int kWiderMergeParts = 32;
 
-template <typename Elem, int D>
-hipError_t launch_merge_d(const DecodeArgs& a, int block_size, hipStream_t stream) {
+template <typename Elem, int D, bool kGroups>
+hipError_t launch_merge_g(const DecodeArgs& a, int block_size, hipStream_t stream) {
   const dim3 grid(unsigned(int64_t(a.num_seqs) * a.num_heads));
   if (a.max_partitions > kWiderMergeParts)
-    return launch(merge_kernel<Elem, D, 16>, grid, dim3(16 * kThreads), 0, stream, a, block_size);
+    return launch(merge_kernel<Elem, D, 16, kGroups>, grid, dim3(16 * kThreads), 0, stream, a,
+                  block_size);
   if (a.max_partitions > kWideMergeParts)
-    return launch(merge_kernel<Elem, D, 4>, grid, dim3(4 * kThreads), 0, stream, a, block_size);
-  return launch(merge_kernel<Elem, D, 1>, grid, dim3(kThreads), 0, stream, a, block_size);
+    return launch(merge_kernel<Elem, D, 4, kGroups>, grid, dim3(4 * kThreads), 0, stream, a,
+                  block_size);
+  return launch(merge_kernel<Elem, D, 1, kGroups>, grid, dim3(kThreads), 0, stream, a, block_size);
+}
+
+template <typename Elem, int D>
+hipError_t launch_merge_d(const DecodeArgs& a, int block_size, hipStream_t stream) {
+  if constexpr (sizeof(Elem) == 2) {  // groups are a bf16 decode path
+    if (a.num_groups > 0) return launch_merge_g<Elem, D, true>(a, block_size, stream);
+  }
+  return launch_merge_g<Elem, D, false>(a, block_size, stream);
 }
 
 template <typename Elem>

@@ -49,6 +49,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "schedule.h"
 
@@ -328,9 +330,201 @@ __device__ __forceinline__ void store_tile_back(const Tile<D>& r, const DecodeAr
   }
 }
 
+// Column tiles of a prefix run: 64 query columns (members x heads) at
+// D <= 128, 32 at D = 256 (their accumulators take D/4 registers each).
+template <int D>
+constexpr int prefix_col_tiles() { return D <= 128 ? 4 : 2; }
+
+// A prefix run: tiles [tin, tin + ntile) of a group's shared tokens, for KV
+// head kvh and the query heads of all the group's served members at once.
+// [P1 共享但不污染状态 and P2 section 2.1: branches of one prompt reference the
+// same physical blocks for their common tokens.]  The shared blocks are read
+// once, through the first member's table, and feed NC column tiles:
+//
+//   S^T[16 tok x 16 col] = K_tile . Q^T     per column tile (16x16x32 bf16)
+//   O^T[D x 16 col]     += V^T_tile . P^T   per column tile (16x16x16 bf16)
+//
+// column c = 16 * ct + (lane & 15) is member c / G, query head c % G of the
+// KV head.  Each column stops at its member's own length (a member shorter
+// than the shared run reads only its tokens).  At the end the run's state is
+// one record per member (o, m, l in the record format of the tail runs) in
+// wide slot `wide`.
+template <int D, int B, bool kStream>
+__device__ __forceinline__ void run_prefix(const DecodeArgs& a, GroupInfo gi, int kvh, int tin,
+                                        int ntile, int64_t wide, int lane, uint32_t k_off,
+                                        uint32_t v_off) {
+  constexpr int NC = prefix_col_tiles<D>();
+  constexpr int KSTEPS = D / 32;
+  constexpr int DCH = D / 16;
+  const int G = a.group;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  gi.first = wave_uniform(gi.first);
+  gi.members = wave_uniform(gi.members);
+  gi.plen = wave_uniform(gi.plen);
+  kvh = wave_uniform(kvh);
+  tin = wave_uniform(tin);
+  ntile = wave_uniform(ntile);
+  wide = wave_uniform64(wide);
+  const int ncols = gi.members * G;
+  const int t_begin = tin * kTile;
+  const int nblk = (gi.plen + B - 1) / B;
+  const int32_t* row = a.block_tables + int64_t(gi.first) * a.max_blocks_per_seq;
+
+  // Q^T operands and column limits.  Columns past the members hold zero
+  // queries and the run's length (never stored).
+  bf16x8_t qop[NC][KSTEPS];
+  int lim[NC];
+  int lane_min = gi.plen;
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+    const int c = ct * 16 + col;
+    const bool used = c < ncols;
+    const int m = used ? c / G : 0;
+    const int hh = used ? c - m * G : 0;
+    const int s = gi.first + m;
+    lim[ct] = used ? min(gi.plen, effective_len(a, s, B)) : gi.plen;
+    lane_min = min(lane_min, lim[ct]);
+    const uint16_t* qh = static_cast<const uint16_t*>(a.q) +
+                         (int64_t(s) * a.num_heads + int64_t(kvh) * G + hh) * D + 8 * grp;
+#pragma unroll
+    for (int j = 0; j < KSTEPS; ++j) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (used) v = *reinterpret_cast<const uint4*>(qh + 32 * j);
+      qop[ct][j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // tiles below every column's limit need no mask
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) lane_min = min(lane_min, __shfl_xor(lane_min, d));
+  const int all_lim = wave_uniform(lane_min);
+
+  floatx4_t acc[NC][DCH];
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) acc[ct][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+  }
+
+  auto t0_of = [&](int k) { return t_begin + k * kTile; };
+
+  auto consume = [&](const Tile<D>& r, int k) {
+    const int t0 = t0_of(k);
+    floatx4_t sacc[NC];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      sacc[ct] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KSTEPS; ++j)
+        sacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, r.k[j]),
+                                                           qop[ct][j], sacc[ct], 0, 0, 0);
+    }
+    short4_t pop[NC];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sacc[ct][i] * a.scale_log2e;
+      if (t0 + kTile > all_lim) {  // some column stops inside this tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = (t0 + 4 * grp + i < lim[ct]) ? x[i] : -INFINITY;
+      }
+      if (r.bad) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = __builtin_nanf("");
+      }
+      const float tmax = colmax4(max_nan(max_nan(x[0], x[1]), max_nan(x[2], x[3])));
+      if (__any(tmax > m_run[ct] + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run[ct], tmax);
+        // a column that has seen no token yet keeps m = -inf and weight 1
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[ct] - m_new);
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int c = 0; c < DCH; ++c) acc[ct][c] *= alpha;
+        m_run[ct] = m_new;
+      }
+      const float m_use = m_run[ct] == -INFINITY ? 0.f : m_run[ct];
+      float pr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(x[i] - m_use);
+      l_run[ct] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      const uint2 pp = make_uint2(pack_bf16x2_rne(pr[0], pr[1]), pack_bf16x2_rne(pr[2], pr[3]));
+      pop[ct] = __builtin_bit_cast(short4_t, pp);
+    }
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) {
+      const short4_t vop = __builtin_bit_cast(short4_t, r.v[c]);
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct)
+        acc[ct][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop[ct], acc[ct][c], 0, 0, 0);
+    }
+  };
+
+  // The tile pipeline of the tail runs (a ring of kRing register tiles, the
+  // block ids from a window of the first member's table), with every tile
+  // whole: the run covers a multiple of 16 tokens.
+  {
+    constexpr int kWin = window_tiles<B>();
+    Tile<D> ring[kRing];
+    int win = load_window(row, t_begin / B, nblk, lane);
+    for (int k0 = 0; k0 < ntile; k0 += kWin) {
+      const int k1 = min(ntile, k0 + kWin);
+      const int wb = t0_of(k0) / B;
+      const int last = k1 - 1;
+      TileIds id;
+#pragma unroll
+      for (int d = 0; d < kRing - 1; ++d) {
+        const int kd = min(k0 + d, last);
+        id = window_ids<B>(win, wb, t0_of(kd), nblk);
+        load_tile<D, B, kStream>(ring[d], a, id, kvh, t0_of(kd), lane, k_off, v_off);
+      }
+      id = window_ids<B>(win, wb, t0_of(min(k0 + kRing - 1, last)), nblk);
+      int nxt = win;
+      if (k1 < ntile) nxt = load_window(row, t0_of(k1) / B, nblk, lane);
+      for (int k = k0; k < k1; k += kRing) {
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) {
+          const int kl = min(k + d + kRing - 1, last);
+          load_tile<D, B, kStream>(ring[(d + kRing - 1) % kRing], a, id, kvh, t0_of(kl), lane,
+                                   k_off, v_off);
+          id = window_ids<B>(win, wb, t0_of(min(k + d + kRing, last)), nblk);
+          if (k + d < k1) consume(ring[d], k + d);
+        }
+      }
+      win = nxt;
+    }
+  }
+
+  // One record per member: o[G][D], m[G], l[G], the stamp.
+  const int rec_f = int(record_floats(G, D));
+  float* wrec = a.ws_wide + wide * a.prefix_members * rec_f;
+#pragma unroll
+  for (int ct = 0; ct < NC; ++ct) {
+    const float l_tot = colsum4(l_run[ct]);
+    const int c = ct * 16 + col;
+    if (c < ncols) {
+      const int m = c / G;
+      const int hh = c - m * G;
+      float* rec = wrec + int64_t(m) * rec_f;
+#pragma unroll
+      for (int cc = 0; cc < DCH; ++cc)
+        *reinterpret_cast<floatx4_t*>(rec + hh * D + 16 * cc + 4 * grp) = acc[ct][cc];
+      if (grp == 0) {
+        rec[G * D + hh] = m_run[ct];
+        rec[G * D + G + hh] = l_tot;
+        if (hh == 0) rec[G * D + 2 * G] = __uint_as_float(a.epoch);
+      }
+    }
+  }
+}
+
 // kParts: some pair has more than one partition, so a run may pass
-// partition ends (split launches only).
-template <int D, int B, bool kSplit, bool kStream, bool kParts>
+// partition ends (split launches only).  kGroups: a grouped line (split
+// launches with shared-prefix groups, schedule.h).
+template <int D, int B, bool kSplit, bool kStream, bool kParts, bool kGroups>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D > 128 || kSplit ? 1 : 2)))
 void decode_bf16_mfma_kernel(DecodeArgs a) {
@@ -446,32 +640,34 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     tb_used = 0;
   };
 
-  // One run: tiles [tin, tin + ntile) of pair (s, kvh).  The tiles of the
-  // pair's partition p make its record k_first + p (stored at
-  // record_slot(slots, k_first + p)), or, when the run is the whole pair (one
-  // partition), go straight to the output.
-  auto run = [&](int s, int kvh, int L, int tin, int ntile, bool whole, PairSlots slots,
-                 int k_first) {
+  // One run: tiles [tin, tin + ntile) of pair (s, kvh), counted from token
+  // tok0 (0, or the tokens of a shared prefix that a prefix unit streams).
+  // The tiles of the pair's partition p make its record k_first + p (stored
+  // at record_slot(slots, k_first + p)), or, when the run is the whole pair
+  // (one partition), go straight to the output.
+  auto run = [&](int s, int kvh, int L, int tok0, int tin, int ntile, bool whole,
+                 PairSlots slots, int k_first) {
     // Every argument is the same in all lanes; say so, so that addresses
     // built from them stay in scalar registers.
     s = wave_uniform(s);
     kvh = wave_uniform(kvh);
     L = wave_uniform(L);
+    tok0 = wave_uniform(tok0);
     tin = wave_uniform(tin);
     ntile = wave_uniform(ntile);
     whole = wave_uniform(int(whole)) != 0;
     slots.fixed = wave_uniform64(slots.fixed);
     slots.overflow = wave_uniform64(slots.overflow);
     k_first = wave_uniform(k_first);
-    const int t_begin = tin * kTile;
-    const int t_end = min(L, (tin + ntile) * kTile);
+    const int t_begin = tok0 + tin * kTile;
+    const int t_end = min(L, tok0 + (tin + ntile) * kTile);
     const int nblk = (L + B - 1) / B;
     const int32_t* row = a.block_tables + int64_t(s) * a.max_blocks_per_seq;
 
     // Appending decode: the run holding the pair's last tile uses the step's
     // row (token L - 1) in that tile and writes the tile back with the row
     // in its slot.
-    const bool append = a.new_k != nullptr && tin + ntile == (L + kTile - 1) / kTile;
+    const bool append = a.new_k != nullptr && tin + ntile == (L - tok0 + kTile - 1) / kTile;
     NewRow<D> nr{};
     int pb_new = 0;
     if (append) {  // issued first: its wait below overlaps the table window's
@@ -661,8 +857,23 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     finish();
   };
 
-  if constexpr (kSplit) {
-    walk_slice_runs(a, B, lane, blockIdx.x, run);
+  if constexpr (kGroups) {
+    __shared__ int4 group_lds[kMaxGroups];
+    const GroupTable gt{group_lds};  // filled by walk_unit_runs
+    walk_unit_runs(a, gt, B, lane, blockIdx.x, [&](const UnitRun& r) {
+      if (r.prefix) {
+        run_prefix<D, B, kStream>(a, group_info(a, gt, r.seq), r.kvh, r.tin, r.ntile, r.wide,
+                                  lane, k_off, v_off);
+      } else {
+        run(r.seq, r.kvh, r.shape.len, r.shape.tok0, r.tin, r.ntile, r.whole, r.slots, r.k0);
+      }
+    });
+    if (staged > 0) drain();
+    if (tb_used > 0) flush_write_backs();
+  } else if constexpr (kSplit) {
+    walk_slice_runs(a, B, lane, blockIdx.x,
+                    [&](int s, int kvh, int L, int tin, int ntile, bool whole, PairSlots slots,
+                        int k_first) { run(s, kvh, L, 0, tin, ntile, whole, slots, k_first); });
     if (staged > 0) drain();
     if (tb_used > 0) flush_write_backs();
   } else {
@@ -677,20 +888,23 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       if (a.lse && lane < G) a.lse[int64_t(s) * a.num_heads + int64_t(kvh) * G + lane] = -INFINITY;
       return;
     }
-    run(s, kvh, L, 0, (L + kTile - 1) / kTile, true, PairSlots{0, 0}, 0);
+    run(s, kvh, L, 0, 0, (L + kTile - 1) / kTile, true, PairSlots{0, 0}, 0);
   }
 }
 
 template <int D, int B, bool kStream>
 hipError_t launch_policy(const DecodeArgs& a, hipStream_t stream) {
+  if (a.split && a.num_groups > 0)
+    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, true, true>,
+                  dim3(unsigned(a.workers)), dim3(kThreads), 0, stream, a);
   if (a.split && a.max_partitions > 1)
-    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, true>, dim3(unsigned(a.workers)),
-                  dim3(kThreads), 0, stream, a);
+    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, true, false>,
+                  dim3(unsigned(a.workers)), dim3(kThreads), 0, stream, a);
   if (a.split)
-    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, false>, dim3(unsigned(a.workers)),
-                  dim3(kThreads), 0, stream, a);
+    return launch(decode_bf16_mfma_kernel<D, B, true, kStream, false, false>,
+                  dim3(unsigned(a.workers)), dim3(kThreads), 0, stream, a);
   const int64_t grid = int64_t(a.num_seqs) * a.num_kv_heads;
-  return launch(decode_bf16_mfma_kernel<D, B, false, kStream, false>, dim3(unsigned(grid)),
+  return launch(decode_bf16_mfma_kernel<D, B, false, kStream, false, false>, dim3(unsigned(grid)),
                 dim3(kThreads), 0, stream, a);
 }
 
@@ -705,9 +919,15 @@ hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
 // from the variant with the most registers, so every variant fits that
 // many workers on the device at once (all split variants use the same LDS).
 template <int D, int B>
-int workers_one() {
+int workers_one(bool groups) {
+  if (groups)  // the grouped kernels: their own occupancy, within the wide region's bound
+    return std::min(kMaxGroupWorkers,
+                    resident_workers(reinterpret_cast<const void*>(
+                                         decode_bf16_mfma_kernel<D, B, true, true, true, true>),
+                                     kThreads));
   return resident_workers(
-      reinterpret_cast<const void*>(decode_bf16_mfma_kernel<D, B, true, true, true>), kThreads);
+      reinterpret_cast<const void*>(decode_bf16_mfma_kernel<D, B, true, true, true, false>),
+      kThreads);
 }
 
 template <int D>
@@ -721,11 +941,11 @@ hipError_t launch_d(const DecodeArgs& a, int block_size, hipStream_t stream) {
 }
 
 template <int D>
-int workers_d(int block_size) {
+int workers_d(int block_size, bool groups) {
   switch (block_size) {
-    case 8: return workers_one<D, 8>();
-    case 16: return workers_one<D, 16>();
-    case 32: return workers_one<D, 32>();
+    case 8: return workers_one<D, 8>(groups);
+    case 16: return workers_one<D, 16>(groups);
+    case 32: return workers_one<D, 32>(groups);
     default: return 0;
   }
 }
@@ -742,11 +962,11 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_
   }
 }
 
-int decode_workers_bf16_mfma(int head_dim, int block_size) {
+int decode_workers_bf16_mfma(int head_dim, int block_size, bool groups) {
   switch (head_dim) {
-    case 64: return workers_d<64>(block_size);
-    case 128: return workers_d<128>(block_size);
-    case 256: return workers_d<256>(block_size);
+    case 64: return workers_d<64>(block_size, groups);
+    case 128: return workers_d<128>(block_size, groups);
+    case 256: return workers_d<256>(block_size, groups);
     default: return 0;
   }
 }

@@ -37,6 +37,25 @@ struct DecodeArgs {
   int32_t split;              // 1: balanced split-KV workers; 0: one wave per (seq, KV head)
   int32_t shared_blocks;      // 1: blocks may be read by several sequences (default-cached loads)
   float scale_log2e;          // scale * log2(e)
+  // Shared-prefix groups (split launches only; num_groups == 0 otherwise).
+  // Group i is sequences group_start[i] .. group_start[i+1] - 1, whose first
+  // prefix_lens[i] tokens sit in the same physical blocks.  The line then
+  // starts with one prefix unit per group (its shared tokens, read once per
+  // KV head for all members' query heads), followed by each sequence's
+  // remaining tokens (schedule.h).
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int32_t num_groups;
+  int32_t prefix_members;     // members of a group a prefix unit serves (its columns / group)
+  float* ws_wide;             // records of prefix pieces: prefix_members records each
+  // Line positions a pair of a grouped line takes beyond its tiles (its run
+  // start: table window, queries, first loads), and per tile of a prefix
+  // unit (whose tiles also feed all members' columns): the balanced cut then
+  // gives every worker about the same time, not the same tile count.
+  int32_t tail_lead;
+  int32_t tail_wt;
+  int32_t prefix_lead;
+  int32_t prefix_wt;
 };
 
 // Arguments of one prefill launch.
@@ -111,7 +130,8 @@ hipError_t launch_decode_bf16_mfma(const DecodeArgs& a, int head_dim, int block_
 // capped at the workspace's worker bound.  0 on failure.  Cached per kernel
 // and device.
 int resident_workers(const void* kernel, int block_threads);
-int decode_workers_bf16_mfma(int head_dim, int block_size);
+// groups: the grouped (shared-prefix) kernel, at most kMaxGroupWorkers.
+int decode_workers_bf16_mfma(int head_dim, int block_size, bool groups = false);
 int decode_workers_simt(int head_dim, bool bf16);
 hipError_t launch_decode_simt(const DecodeArgs& a, int head_dim, int block_size, bool bf16,
                               hipStream_t stream);

@@ -212,3 +212,169 @@ def test_double_floor_division_is_exact_below_2_53():
             cases += [(n * w, w), (n * w - 1, n), ((n - 1 + 1) * w - 1, n)]
     for p, q in cases:
         assert math.floor(float(p) / float(q)) == p // q, (p, q)
+
+
+# ---------------------------------------------------------------- grouped lines
+
+def _group_info(group_start, prefix_lens, lengths, members_cap, i):
+    S = len(lengths)
+    s0 = min(max(int(group_start[i]), 0), S)
+    s1 = min(max(int(group_start[i + 1]), 0), S)
+    members = max(0, min(s1 - s0, members_cap))
+    plen = 0
+    if members > 0:
+        plen = min(max(int(prefix_lens[i]), 0), int(lengths[s0])) // 16 * 16
+    return s0, members, plen
+
+
+def _seq_prefix(group_start, prefix_lens, lengths, members_cap, s):
+    n = len(prefix_lens)
+    if n == 0 or group_start[0] > s:
+        return 0, -1, -1
+    lo, hi = 0, n - 1
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if group_start[mid] <= s:
+            lo = mid
+        else:
+            hi = mid - 1
+    first, members, plen = _group_info(group_start, prefix_lens, lengths, members_cap, lo)
+    m = s - first
+    if m < 0 or m >= members:
+        return 0, -1, -1
+    return min(plen, int(lengths[s])), lo, m
+
+
+def _unit_shapes(group_start, prefix_lens, lengths, members_cap, partition, tail_lead=0,
+                 prefix_lead=0, prefix_wt=1, tail_wt=1):
+    """(tiles, parts, tok0, lead, wt, span) of every unit: prefix units, then
+    tails.  A pair takes span = lead + tiles * wt line positions (0 without
+    tiles); tile t sits at lead + t * wt from the pair's start."""
+    units = []
+    for i in range(len(prefix_lens)):
+        _, _, plen = _group_info(group_start, prefix_lens, lengths, members_cap, i)
+        t = plen // TILE
+        units.append((t, 0, 0, prefix_lead, prefix_wt, prefix_lead + t * prefix_wt if t else 0))
+    for s, L in enumerate(lengths):
+        t0, _, _ = _seq_prefix(group_start, prefix_lens, lengths, members_cap, s)
+        n = int(L) - t0
+        t = -(-n // TILE)
+        units.append((t, -(-n // partition), t0, tail_lead, tail_wt,
+                      tail_lead + t * tail_wt if t else 0))
+    return units
+
+
+def grouped_pieces(group_start, prefix_lens, lengths, hkv, partition, workers, members_cap,
+                   tail_lead=0, prefix_lead=0, prefix_wt=1, tail_wt=1):
+    units = _unit_shapes(group_start, prefix_lens, lengths, members_cap, partition, tail_lead,
+                         prefix_lead, prefix_wt, tail_wt)
+    ng = len(prefix_lens)
+    spans = [u[5] for u in units]
+    parts = [u[1] for u in units]
+    pref_t = np.concatenate([[0], np.cumsum(spans)]).astype(np.int64)
+    pref_p = np.concatenate([[0], np.cumsum(parts)]).astype(np.int64)
+    n = int(pref_t[-1]) * hkv
+    tpp = partition // TILE
+    out = []
+    for b in range(workers if n else 0):
+        x0, x1 = slice_start(n, workers, b), slice_start(n, workers, b + 1)
+        cur = x0
+        while cur < x1:
+            u = int(np.searchsorted(pref_t * hkv, cur, side="right") - 1)
+            while spans[u] == 0:
+                u += 1
+            tiles, _, tok0, lead, wt, span = units[u]
+            ubase = int(pref_t[u]) * hkv
+            g = (cur - ubase) // span
+            pair_base = ubase + g * span
+            end = min(pair_base + span, x1)
+            first_pos = pair_base + lead
+            tin = 0 if cur <= first_pos else -(-(cur - first_pos) // wt)
+            tend = 0 if end <= first_pos else min(tiles, -(-(end - first_pos) // wt))
+            b_first = owner_of(n, workers, first_pos)
+            t = tin
+            while t < tend:  # tail runs are cut further at partition ends
+                if u < ng:
+                    out.append(("prefix", b, u, g, t, tend - t, u * hkv + g + b))
+                    break
+                part = t // tpp
+                e = min(tend, (part + 1) * tpp)
+                k = part + b - b_first
+                slot = ((u - ng) * hkv + g) * PAIR_SLOTS + k if k < PAIR_SLOTS else \
+                    len(lengths) * hkv * PAIR_SLOTS + int(pref_p[u]) * hkv + g * parts[u] + \
+                    b_first + k
+                whole = tin == 0 and tend == tiles and parts[u] == 1 and tok0 == 0
+                out.append(("tail", b, u, g, t, e - t, None if whole else slot))
+                t = e
+            cur = end
+    return out, n, units, pref_t, pref_p
+
+
+@pytest.mark.parametrize("weights", [(0, 0, 1, 1), (4, 0, 1, 1), (3, 2, 2, 1), (1, 0, 3, 1),
+                                     (14, 14, 5, 4), (14, 0, 5, 4), (23, 52, 6, 4)])
+@pytest.mark.parametrize("seed", range(12))
+def test_grouped_line_covers_and_indexes(seed, weights):
+    tail_lead, prefix_lead, prefix_wt, tail_wt = weights
+    rng = np.random.default_rng(seed)
+    hkv = int(rng.choice([1, 2, 8]))
+    G = int(rng.choice([1, 4, 8, 16]))
+    members_cap = 64 // G
+    partition = int(rng.choice([16, 32, 512]))
+    workers = int(rng.choice([1, 3, 64, 768, 1024]))
+    sizes = rng.integers(0, 20, size=int(rng.integers(0, 6)))
+    group_start = np.concatenate([[int(rng.integers(0, 3))], np.cumsum(sizes) +
+                                  int(rng.integers(0, 3))]).astype(np.int64)
+    S = int(group_start[-1] + rng.integers(0, 4))
+    lengths = rng.integers(0, 700, size=S)
+    prefix_lens = rng.integers(-5, 600, size=len(sizes))
+    ps, n, units, pref_t, pref_p = grouped_pieces(group_start, prefix_lens, lengths, hkv,
+                                                  partition, workers, members_cap, tail_lead,
+                                                  prefix_lead, prefix_wt, tail_wt)
+    ng = len(prefix_lens)
+    # every tile of every unit and KV head exactly once
+    seen = {}
+    for kind, b, u, g, tin, nt, slot in ps:
+        for t in range(tin, tin + nt):
+            assert (u, g, t) not in seen
+            seen[(u, g, t)] = b
+    assert len(seen) == sum(u[0] for u in units) * hkv
+    for (u, g, t), b in seen.items():  # a tile belongs to the owner of its position
+        tiles, _, _, lead, wt, span = units[u]
+        assert b == owner_of(n, workers, int(pref_t[u]) * hkv + g * span + lead + t * wt)
+    # each member's tokens: the prefix unit's plus its tail's
+    for s, L in enumerate(lengths):
+        t0, grp, m = _seq_prefix(group_start, prefix_lens, lengths, members_cap, s)
+        tail = units[ng + s]
+        assert tail[2] == t0 and t0 + tail[0] * TILE >= L > t0 + (tail[0] - 1) * TILE - 1 \
+            if tail[0] else L == t0
+        if grp >= 0:
+            assert t0 == min(units[grp][0] * TILE, int(L))
+    # wide slots distinct, within the wide region, and in the merge's range
+    wide = [p for p in ps if p[0] == "prefix"]
+    slots = [p[6] for p in wide]
+    assert len(set(slots)) == len(slots)
+    assert all(0 <= x < ng * hkv + workers for x in slots)
+    for kind, b, u, g, tin, nt, slot in wide:
+        tiles, _, _, lead, wt, span = units[u]
+        base = int(pref_t[u]) * hkv + g * span + lead
+        bf, bl = owner_of(n, workers, base), owner_of(n, workers, base + (tiles - 1) * wt)
+        assert u * hkv + g + bf <= slot <= u * hkv + g + bl
+    # tail records distinct, within the record region, and each in the
+    # merge's range for its pair (k < parts + b_last - b_first)
+    recs = [p for p in ps if p[0] == "tail" and p[6] is not None]
+    assert len(set(p[6] for p in recs)) == len(recs)
+    max_parts = max(1, -(-int(lengths.max(initial=0)) // partition))
+    assert all(0 <= p[6] < S * hkv * (PAIR_SLOTS + max_parts) + workers for p in recs)
+    for kind, b, u, g, tin, nt, slot in recs:
+        tiles, parts, _, lead, wt, span = units[u]
+        base = int(pref_t[u]) * hkv + g * span + lead
+        bf, bl = owner_of(n, workers, base), owner_of(n, workers, base + (tiles - 1) * wt)
+        k = tin // (partition // TILE) + b - bf
+        assert 0 <= k < parts + bl - bf
+    # whole pairs: one worker owns every tile, and the merge agrees
+    for kind, b, u, g, tin, nt, slot in ps:
+        if kind == "tail" and slot is None:
+            tiles, parts, tok0, lead, wt, span = units[u]
+            base = int(pref_t[u]) * hkv + g * span + lead
+            assert owner_of(n, workers, base) == owner_of(n, workers, base + (tiles - 1) * wt)
+            assert parts == 1 and tok0 == 0

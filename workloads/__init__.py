@@ -14,6 +14,7 @@ from .generate import (  # noqa: F401
     llama3_8b_decode,
     long_context,
     shared_prefix,
+    shared_groups,
     mixed_lengths,
     custom,
     normal_values,

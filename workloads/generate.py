@@ -58,6 +58,7 @@ __all__ = [
     "llama3_8b_decode",
     "long_context",
     "shared_prefix",
+    "shared_groups",
     "mixed_lengths",
     "custom",
     "PrefillWorkload",
@@ -441,6 +442,60 @@ def shared_prefix(phase: str = "steady", seed: int = 307_004, num_groups: int = 
                      hist_seq=np.concatenate(hist_seq), hist_pos=np.concatenate(hist_pos),
                      copy_pairs=np.array(copies, np.int64).reshape(-1, 2), extra=extra,
                      hist_data=(hist_key, hist_value))
+
+
+def shared_groups(spec, num_heads, num_kv_heads, head_dim, block_size, dtype="bf16",
+                  seed=307_120, pool_factor=1.25, name="shared_groups") -> Workload:
+    """Sequences that share the blocks of a common prefix, group by group.
+
+    ``spec`` is a list of ``(shared_tokens, tails)``: one group per entry,
+    whose ``len(tails)`` members are consecutive in the batch and share the
+    physical blocks of their first ``shared_tokens`` tokens (a multiple of
+    the block size; 0 = no sharing), member ``i`` then owning ``tails[i] >= 1``
+    more tokens (the step's token among them) in private blocks.  The shared
+    tokens are written once, through the group's first member.  ``extra``
+    holds ``group_start`` (int32 ``[groups + 1]``) and ``shared_tokens``
+    (int32 ``[groups]``)."""
+    st = _streams(seed)
+    B = int(block_size)
+    lengths, group_start, shared = [], [0], []
+    for sh, tails in spec:
+        if sh % B:
+            raise ValueError("shared tokens must fill whole blocks")
+        if any(int(t) < 1 for t in tails):
+            raise ValueError("every member owns at least the step's token")
+        lengths += [sh + int(t) for t in tails]
+        group_start.append(len(lengths))
+        shared.append(sh)
+    need = sum(sh // B + sum(_blocks_to_hold(int(t), B) for t in tails) for sh, tails in spec)
+    NB = max(_pool_size(need, pool_factor), 1)
+    pool = _Pool(NB, np.random.Generator(np.random.PCG64(st["perm"])).permutation(NB))
+    rows, hist_seq, hist_pos, src = [], [], [], []
+    s = 0
+    for gi, (sh, tails) in enumerate(spec):
+        common = pool.take(sh // B)
+        if sh:  # written once, through the first member
+            hist_seq.append(np.full(sh, s, np.int32))
+            hist_pos.append(np.arange(sh, dtype=np.int32))
+            src.append(("shared", gi, sh))
+        for t in tails:
+            rows.append(common + pool.take(_blocks_to_hold(int(t), B)))
+            if int(t) > 1:
+                hist_seq.append(np.full(int(t) - 1, s, np.int32))
+                hist_pos.append(np.arange(sh, sh + int(t) - 1, dtype=np.int32))
+                src.append(("own", s, int(t) - 1))
+            s += 1
+    Hkv, D = num_kv_heads, head_dim
+    n_hist = sum(x[2] for x in src)
+    hist = _normal(st["hist"], (2, n_hist, Hkv, D), dtype)
+    MB = max(1, max(len(r) for r in rows))
+    extra = {"group_start": np.array(group_start, np.int32),
+             "shared_tokens": np.array(shared, np.int32)}
+    return _assemble(name, dtype, lengths, rows, rows, num_heads, num_kv_heads, head_dim, B, NB,
+                     MB, st,
+                     hist_seq=np.concatenate(hist_seq) if hist_seq else np.zeros(0, np.int32),
+                     hist_pos=np.concatenate(hist_pos) if hist_pos else np.zeros(0, np.int32),
+                     extra=extra, hist_data=(hist[0], hist[1]))
 
 
 def mixed_lengths(block_size: int = 16, seed: int = 307_005, num_seqs: int = 256,
