@@ -218,10 +218,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
  * the last block past L_s are never used (they may hold anything, NaN
  * included).  Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED /
  * PA_ERR_WORKSPACE on a failed check; with partition_size > 0,
- * PA_ERR_UNSUPPORTED also when num_seqs * ceil(max_context_len / 16)
- * exceeds 2^31 - 1 or, times num_kv_heads, reaches 2^40 (the split schedule
- * counts tiles per KV head in 32-bit integers and divides line positions in
- * doubles).
+ * PA_ERR_UNSUPPORTED also when num_seqs * (4 * ceil(max_context_len / 16)
+ * + 12) exceeds 2^31 - 1 or, times num_kv_heads, reaches 2^40 (the split
+ * schedule places each 16-token tile at 4 line positions and each
+ * (sequence, KV head) run start at 12, counts positions per KV head in
+ * 32-bit integers and divides them in doubles).
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,

@@ -129,16 +129,22 @@ constexpr int kTailLead = 23;
 constexpr int kPrefixWt = 6;
 constexpr int kPrefixLead = 52;
 
-void set_group_weights(DecodeArgs& a) {
-  a.tail_lead = kTailLead;
-  a.tail_wt = kTailWt;
+// Line weights of a plain split launch, in the same quarter tiles: a tile
+// 4, a run's start 12.
+constexpr int kPlainWt = 4;
+constexpr int kPlainLead = 12;
+
+void set_line_weights(DecodeArgs& a, bool groups) {
+  a.tail_lead = groups ? kTailLead : kPlainLead;
+  a.tail_wt = groups ? kTailWt : kPlainWt;
   a.prefix_lead = kPrefixLead;
   a.prefix_wt = kPrefixWt;
 }
 
-// Longest context the split-schedule size check should assume for a grouped
-// line: a pair's positions are its tiles times the heavier weight plus a lead.
-int64_t weighted_len(int64_t max_len) {
+// Longest context the split-schedule size check should assume: a pair's
+// positions are its tiles times the heaviest weight plus a lead.
+int64_t weighted_len(int64_t max_len, bool groups) {
+  if (!groups) return max_len * kPlainWt + 16 * int64_t(kPlainLead);
   const int wt = kPrefixWt > kTailWt ? kPrefixWt : kTailWt;
   const int lead = kTailLead > kPrefixLead ? kTailLead : kPrefixLead;
   return max_len * wt + 16 * int64_t(lead);
@@ -202,8 +208,7 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
   // in 32-bit integers and divides line positions (tiles x KV heads) times
   // workers in doubles
   if (partition_size > 0 &&
-      !split_line_fits(num_seqs + num_groups, num_kv_heads,
-                       num_groups > 0 ? weighted_len(max_len) : max_len))
+      !split_line_fits(num_seqs + num_groups, num_kv_heads, weighted_len(max_len, num_groups > 0)))
     return PA_ERR_UNSUPPORTED;
   DecodeArgs& a = plan->args;
   plan->split = partition_size > 0;
@@ -231,8 +236,8 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
       a.prefix_lens = prefix_lens;
       a.num_groups = num_groups;
       a.prefix_members = prefix_members_for(head_dim, group);
-      set_group_weights(a);
     }
+    set_line_weights(a, groups);
     a.workers = workers;
     a.partition_size = partition_size;
     a.max_partitions = int32_t(parts);
@@ -322,8 +327,7 @@ int merge_call(void* out, const int32_t* context_lens, const int32_t* group_star
   if (!workspace || !aligned16(workspace) || int64_t(workspace_bytes) < need)
     return PA_ERR_WORKSPACE;
   if (int64_t(num_seqs) * num_heads > 0x7FFFFFFF) return PA_ERR_UNSUPPORTED;
-  if (!split_line_fits(num_seqs + num_groups, num_kv_heads,
-                       num_groups > 0 ? weighted_len(max_len) : max_len))
+  if (!split_line_fits(num_seqs + num_groups, num_kv_heads, weighted_len(max_len, num_groups > 0)))
     return PA_ERR_UNSUPPORTED;
   const bool bf16 = dtype == PA_DTYPE_BF16;
   const bool groups = num_groups > 0 && bf16;
@@ -343,8 +347,8 @@ int merge_call(void* out, const int32_t* context_lens, const int32_t* group_star
     a.prefix_lens = prefix_lens;
     a.num_groups = num_groups;
     a.prefix_members = prefix_members_for(head_dim, group);
-    set_group_weights(a);
   }
+  set_line_weights(a, groups);
   a.workers = workers;
   a.split = 1;
   a.num_seqs = num_seqs;

@@ -77,15 +77,22 @@ __device__ __forceinline__ int owner_of(int64_t n, int workers, int64_t x) {
   return int(floor_div_small((x + 1) * workers - 1, n));
 }
 
+// A pair's place on the line: `span` positions, `lead` of them for its run
+// start, then `wt` per tile (tile t at lead + t * wt from the pair's start),
+// so that the equal cut of positions gives workers equal time rather than
+// equal tiles (a run's start costs dependent memory round trips).  The
+// weights come from the launch (DecodeArgs::tail_lead, tail_wt).
 struct PairShape {
   int tiles;   // T_s
   int parts;   // nparts_s
+  int span;    // positions of one pair: tail_lead + tiles * tail_wt, or 0
 };
 
 __device__ __forceinline__ PairShape shape_of_len(const DecodeArgs& a, int L) {
   PairShape p;
   p.tiles = (L + 15) / 16;
   p.parts = (L + a.partition_size - 1) / a.partition_size;
+  p.span = p.tiles > 0 ? a.tail_lead + p.tiles * a.tail_wt : 0;
   return p;
 }
 
@@ -127,7 +134,7 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
   int lt = 0, lp = 0;
   for (int s = first; s < last; ++s) {
     const PairShape ps = pair_shape(a, s, block_size);
-    lt += ps.tiles;
+    lt += ps.span;
     lp += ps.parts;
   }
   const int it = wave_inclusive_scan(lt, lane);
@@ -148,13 +155,13 @@ __device__ __forceinline__ Slice locate_slice(const DecodeArgs& a, int block_siz
       meta[s] = int32_t(ct);
       meta[S + s] = int32_t(cp);
     }
-    if (ps.tiles > 0 && r.x0 >= ct * a.num_kv_heads && r.x0 < (ct + ps.tiles) * a.num_kv_heads) {
+    if (ps.span > 0 && r.x0 >= ct * a.num_kv_heads && r.x0 < (ct + ps.span) * a.num_kv_heads) {
       found_s = s;
       found_len = len;
       found_t = ct;
       found_p = cp;
     }
-    ct += ps.tiles;
+    ct += ps.span;
     cp += ps.parts;
   }
   if (publish && lane == 0) {
@@ -192,10 +199,11 @@ __device__ __forceinline__ void walk_slice_runs(const DecodeArgs& a, int block_s
   int len = sl.len;
   int len_next = s + 1 < a.num_seqs ? effective_len(a, s + 1, block_size) : 0;
   PairShape ps = shape_of_len(a, len);
+  const int lead = a.tail_lead, wt = a.tail_wt;
   int64_t cur = sl.x0;
   while (cur < sl.x1) {
-    if (cur >= sbase + int64_t(Hkv) * ps.tiles) {
-      sbase += int64_t(Hkv) * ps.tiles;
+    if (cur >= sbase + int64_t(Hkv) * ps.span) {
+      sbase += int64_t(Hkv) * ps.span;
       gpb += int64_t(Hkv) * ps.parts;
       ++s;
       len = len_next;
@@ -204,18 +212,22 @@ __device__ __forceinline__ void walk_slice_runs(const DecodeArgs& a, int block_s
       continue;
     }
     const int64_t off = cur - sbase;
-    const int g = int(off / ps.tiles);
-    const int tin = int(off - int64_t(g) * ps.tiles);
-    const int64_t end = min(sbase + int64_t(g + 1) * ps.tiles, sl.x1);
-    const int ntile = int(end - cur);
+    const int g = int(off / ps.span);
+    const int64_t pair_base = sbase + int64_t(g) * ps.span;
+    const int64_t end = min(pair_base + ps.span, sl.x1);
+    // tiles whose positions pair_base + lead + t * wt lie in [cur, end)
+    const int64_t first_pos = pair_base + lead;
+    const int tin = cur <= first_pos ? 0 : int((cur - first_pos + wt - 1) / wt);
+    const int tend = end <= first_pos ? 0 : min(ps.tiles, int((end - first_pos + wt - 1) / wt));
+    cur = end;
+    if (tend <= tin) continue;  // only the pair's lead (or between tiles) in this slice
+    const int ntile = tend - tin;
     const bool whole = tin == 0 && ntile == ps.tiles && ps.parts == 1;
-    const int64_t pair_base = sbase + int64_t(g) * ps.tiles;
-    const int b_first = owner_of(sl.n, a.workers, pair_base);
+    const int b_first = owner_of(sl.n, a.workers, first_pos);
     PairSlots slots;
     slots.fixed = (int64_t(s) * Hkv + g) * kPairSlots;
     slots.overflow = int64_t(a.num_seqs) * Hkv * kPairSlots + gpb + int64_t(g) * ps.parts + b_first;
     run(s, g, len, tin, ntile, whole, slots, b - b_first);
-    cur = end;
   }
 }
 
@@ -272,10 +284,10 @@ __device__ __forceinline__ bool pair_records(const DecodeArgs& a, int block_size
   const PairShape ps = pair_shape(a, s, block_size);
   if (ps.tiles == 0) return false;
   const int Hkv = a.num_kv_heads;
-  const int64_t base = int64_t(pref_t) * Hkv + int64_t(g) * ps.tiles;
+  const int64_t base = int64_t(pref_t) * Hkv + int64_t(g) * ps.span + a.tail_lead;
   const int64_t gp0 = int64_t(pref_p) * Hkv + int64_t(g) * ps.parts;
   const int b_first = owner_of(n, a.workers, base);
-  const int b_last = owner_of(n, a.workers, base + ps.tiles - 1);
+  const int b_last = owner_of(n, a.workers, base + int64_t(ps.tiles - 1) * a.tail_wt);
   pr->slots.fixed = pair_fixed_slot(a, s, g);
   pr->slots.overflow = int64_t(a.num_seqs) * Hkv * kPairSlots + gp0 + b_first;
   pr->count = ps.parts + b_last - b_first;

@@ -39,11 +39,15 @@ def owner_of(n, workers, x):
     return ((x + 1) * workers - 1) // n
 
 
-def pieces(lengths, hkv, partition, workers):
-    """All pieces, as (worker, s, g, first tile, tiles, whole, record)."""
+def pieces(lengths, hkv, partition, workers, lead=0, wt=1):
+    """All pieces, as (worker, s, g, first tile, tiles, whole, record).  A
+    pair takes span = lead + tiles * wt line positions (0 without tiles);
+    its tile t sits at lead + t * wt from the pair's start, owned by the
+    worker whose slice holds that position."""
     tiles = [-(-int(L) // TILE) for L in lengths]
     parts = [-(-int(L) // partition) for L in lengths]
-    pref_t = np.concatenate([[0], np.cumsum(tiles)])
+    spans = [lead + t * wt if t else 0 for t in tiles]
+    pref_t = np.concatenate([[0], np.cumsum(spans)]).astype(np.int64)
     pref_p = np.concatenate([[0], np.cumsum(parts)])
     n = int(pref_t[-1]) * hkv
     tpp = partition // TILE
@@ -55,30 +59,37 @@ def pieces(lengths, hkv, partition, workers):
         cur = x0
         while cur < x1:
             s = int(np.searchsorted(pref_t * hkv, cur, side="right") - 1)
-            while tiles[s] == 0:  # sequences with no tiles own no line positions
+            while spans[s] == 0:  # sequences with no tiles own no line positions
                 s += 1
             sbase = int(pref_t[s]) * hkv
-            off = cur - sbase
-            g, tin = divmod(off, tiles[s])
-            part = tin // tpp
-            end = min(sbase + (g + 1) * tiles[s], sbase + g * tiles[s] + (part + 1) * tpp, x1)
-            ntile = end - cur
-            whole = tin == 0 and ntile == tiles[s]
-            rec = int(pref_p[s]) * hkv + g * parts[s] + part + b
-            out.append((b, s, g, tin, ntile, whole, rec))
+            g = (cur - sbase) // spans[s]
+            pair_base = sbase + g * spans[s]
+            end = min(pair_base + spans[s], x1)
+            first_pos = pair_base + lead
+            tin = 0 if cur <= first_pos else -(-(cur - first_pos) // wt)
+            tend = 0 if end <= first_pos else min(tiles[s], -(-(end - first_pos) // wt))
+            t = tin
+            while t < tend:
+                part = t // tpp
+                e = min(tend, (part + 1) * tpp)
+                whole = tin == 0 and tend == tiles[s] and parts[s] == 1
+                rec = int(pref_p[s]) * hkv + g * parts[s] + part + b
+                out.append((b, s, g, t, e - t, whole, rec))
+                t = e
             cur = end
     return out, n
 
 
-def merge_range(lengths, hkv, partition, workers, n, s, g):
+def merge_range(lengths, hkv, partition, workers, n, s, g, lead=0, wt=1):
     tiles = [-(-int(L) // TILE) for L in lengths]
     parts = [-(-int(L) // partition) for L in lengths]
-    pref_t = int(sum(tiles[:s]))
+    spans = [lead + t * wt if t else 0 for t in tiles]
+    pref_t = int(sum(spans[:s]))
     pref_p = int(sum(parts[:s]))
-    base = pref_t * hkv + g * tiles[s]
+    base = pref_t * hkv + g * spans[s] + lead
     gp0 = pref_p * hkv + g * parts[s]
     b_first = owner_of(n, workers, base)
-    b_last = owner_of(n, workers, base + tiles[s] - 1)
+    b_last = owner_of(n, workers, base + (tiles[s] - 1) * wt)
     return gp0 + b_first, gp0 + parts[s] - 1 + b_last, b_first == b_last and parts[s] == 1
 
 
@@ -107,10 +118,12 @@ def random_cases():
     return out
 
 
+@pytest.mark.parametrize("weights", [(0, 1), (12, 4), (3, 2)])
 @pytest.mark.parametrize("case", CASES + random_cases())
-def test_schedule_invariants(case):
+def test_schedule_invariants(case, weights):
     lengths, hkv, partition, workers = case
-    ps, n = pieces(lengths, hkv, partition, workers)
+    lead, wt = weights
+    ps, n = pieces(lengths, hkv, partition, workers, lead, wt)
     tiles = [-(-int(L) // TILE) for L in lengths]
     parts = [-(-int(L) // partition) for L in lengths]
 
@@ -140,7 +153,7 @@ def test_schedule_invariants(case):
         if tiles[s] == 0:
             continue
         for g in range(hkv):
-            first, last, whole = merge_range(lengths, hkv, partition, workers, n, s, g)
+            first, last, whole = merge_range(lengths, hkv, partition, workers, n, s, g, lead, wt)
             mine = [r for r, ss, gg in recs if (ss, gg) == (s, g)]
             n_pieces = sum(1 for p in ps if (p[1], p[2]) == (s, g))
             assert whole == (n_pieces == 1)
@@ -157,7 +170,7 @@ def test_schedule_invariants(case):
     S = len(lengths)
     slot_of = {}
     for r, s_, g_ in recs:
-        first, last, _ = merge_range(lengths, hkv, partition, workers, n, s_, g_)
+        first, last, _ = merge_range(lengths, hkv, partition, workers, n, s_, g_, lead, wt)
         k = r - first
         assert 0 <= k <= last - first
         slot_of[r] = (s_ * hkv + g_) * PAIR_SLOTS + k if k < PAIR_SLOTS else S * hkv * PAIR_SLOTS + r
@@ -169,7 +182,7 @@ def test_schedule_invariants(case):
         if tiles[s] == 0:
             continue
         for g in range(hkv):
-            first, last, whole = merge_range(lengths, hkv, partition, workers, n, s, g)
+            first, last, whole = merge_range(lengths, hkv, partition, workers, n, s, g, lead, wt)
             if whole:
                 continue
             seen_recs = set()
