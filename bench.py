@@ -51,28 +51,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 # HBM bytes per launch of the dominant kernel, from two rocprofv3 --pmc passes
-# (FETCH_SIZE, then WRITE_SIZE) over this script's default run, each scaled by
-# what the same counter reads for pa_copy_blocks on a known byte count (run
-# with --copy-calibration): FETCH_SIZE x 1.99187, WRITE_SIZE x 1.0.  Summary
-# and commands: profiles/append_decode_partials_llama3_8b_decode_hbm_bytes.md.  The
-# figure holds only for the kernel sources it was measured with.
+# (FETCH_SIZE, then WRITE_SIZE) over this script's run of each workload, each
+# scaled by what the same counter reads for pa_copy_blocks on a known byte
+# count (run with --copy-calibration): FETCH_SIZE x 1.99183, WRITE_SIZE x 1.0.
+# Summaries and commands: profiles/copy_blocks_calibration_hbm_bytes.md and
+# the profiles/*_hbm_bytes.md file of each workload.  Keyed by (workload,
+# partition, appending step, shared-block loads, prefix groups); the figures
+# hold only for the kernel sources they were measured with (their hash).
 KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache_307_amd/csrc/schedule.h",
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
+MEASURED_TRAFFIC_SHA256 = "a52214b290edce72378fb32f255697593327931b832bae0471c39d6b306f217b"
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False, False): {
-        "bytes": 553867967, "fetch_bytes": 549001823, "write_bytes": 4866144,
-        "sources_sha256": "6f946f039748493493f0909c691cea37e47ddb3517aa81b8a2104a1b97bee7fe"},
+        "bytes": 554206757, "fetch_bytes": 549378693, "write_bytes": 4828064},
+    ("long_context", 512, True, False, False): {
+        "bytes": 2719684712, "fetch_bytes": 2696345049, "write_bytes": 23339663},
+    ("shared_prefix_steady", 4096, True, False, True): {
+        "bytes": 480513915, "fetch_bytes": 453780065, "write_bytes": 26733850},
+    ("shared_prefix_fork", 4096, True, False, True): {
+        "bytes": 210932490, "fetch_bytes": 177702101, "write_bytes": 33230389},
+    ("mixed_lengths_B8", 8192, True, False, False): {
+        "bytes": 1659308740, "fetch_bytes": 1645859366, "write_bytes": 13449374},
+    ("mixed_lengths_B16", 8192, True, False, False): {
+        "bytes": 1661506045, "fetch_bytes": 1643862382, "write_bytes": 17643663},
+    ("mixed_lengths_B32", 8192, True, False, False): {
+        "bytes": 1642828211, "fetch_bytes": 1625184166, "write_bytes": 17644045},
 }
 # The same two passes over `bench.py --workload llama3_8b_prefill` for
 # pa_prefill (summary: profiles/prefill_llama3_8b_prefill_hbm_bytes.md).
 PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_307_amd/csrc/device_common.h",
                    "paged_kv_cache_307_amd/csrc/internal.h", "paged_kv_cache_307_amd/csrc/api.hip",
                    "paged_kv_cache_307_amd/build.py"]
+PREFILL_TRAFFIC_SHA256 = "7659e35804cfd172d62ced01be6b8c956ab3a7b05084c3911ba67a3c1e0af165"
 PREFILL_TRAFFIC = {
-    "llama3_8b_prefill": {
-        "bytes": 297528224, "fetch_bytes": 230396448, "write_bytes": 67131776,
-        "sources_sha256": "5a0f4639d7762fb380971ef827c03c6c31c8134098f6c04ba437579488ed8dd8"},
+    "llama3_8b_prefill": {"bytes": 297493969, "fetch_bytes": 230361468, "write_bytes": 67132501},
 }
 
 
@@ -171,7 +184,7 @@ def measured_traffic(workload, partition, append, shared, groups=False):
     """Counter-derived HBM bytes per launch, or None when there is no
     measurement for this workload and step or the kernel changed since."""
     rec = MEASURED_TRAFFIC.get((workload, partition, append, shared, groups))
-    if rec is None or rec["sources_sha256"] != kernel_sources_sha256():
+    if rec is None or MEASURED_TRAFFIC_SHA256 != kernel_sources_sha256():
         return None
     return rec["bytes"]
 
@@ -378,7 +391,7 @@ def prefill_traffic(workload):
     """Counter-derived HBM bytes per pa_prefill launch, or None when there is
     no measurement or the kernel changed since."""
     rec = PREFILL_TRAFFIC.get(workload)
-    if rec is None or rec["sources_sha256"] != kernel_sources_sha256(PREFILL_SOURCES):
+    if rec is None or PREFILL_TRAFFIC_SHA256 != kernel_sources_sha256(PREFILL_SOURCES):
         return None
     return rec["bytes"]
 
@@ -502,7 +515,7 @@ def run_prefill_bench(args):
         "query_tokens_per_s": round(w.num_query_tokens / (ms_per_step * 1e-3), 1),
         "flops_per_step": F,
         "roofline": {
-            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 1 wave per workgroup, Q in LDS, P.V on 32x32x16 (pa_prefill)", "bound": "mfma",
+            "kernel": "prefill_bf16_mfma_kernel<128,16,4,2>, 1 wave per workgroup, Q in LDS, S on 16x16x32, P.V on 32x32x16 (pa_prefill)", "bound": "mfma",
             "achieved": round(k_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(k_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "avg_us": round(attend_ms * 1e3, 3),
             "flops_per_launch": F, "traffic": prefill_traffic(w.name),

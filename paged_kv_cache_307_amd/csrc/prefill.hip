@@ -18,18 +18,20 @@
 // tiles
 //
 //   S^T[16 tok x 16 col] = K_tile[16 tok x D] . Q^T[D x 16 col]   (16x16x32 bf16)
-//   O^T[D x 16 col]     += V^T_tile[D x 16 tok] . P^T[16 tok x 16 col] (16x16x16 bf16)
+//   O^T[32 dim x 32 col] += V^T_tile[32 dim x 16 tok] . P^T[16 tok x 32 col]
+//                                   (32x32x16 bf16, column tiles taken in pairs)
 //
-// with the operand layouts of the decode kernel (lane l: row/column l & 15,
-// group l >> 4; K rows are 16-byte loads from the [B][D] tile, V columns
-// 8-byte loads from the token-innermost [D][B] tile), so each K/V tile feeds
-// NC products of each kind.  Column c sees tokens below its own limit
-// lim_c = L - n + i_c + 1; tiles below the smallest limit of the wave need
-// no mask.  Block ids are scalar loads fetched one tile ahead of the tile
-// loads.  A workgroup is one wave; the launch order keeps all row groups of
-// one (sequence, KV head) on one XCD (workgroup i runs on XCD i % 8), latest
-// positions first, so the re-reads of a tile by other row groups hit that
-// XCD's L2.
+// S^T has the operand layout of the decode kernel (lane l: row/column l & 15,
+// group l >> 4; K rows are 16-byte loads from the [B][D] tile); P^T of two
+// column tiles is rearranged by one lane swap into the 32x32 product's
+// operand, whose V^T rows are 16-byte loads from the token-innermost [D][B]
+// tile.  Each K/V tile thus feeds NC products of each kind.  Column c sees
+// tokens below its own limit lim_c = L - n + i_c + 1; tiles below the
+// smallest limit of the wave need no mask.  Block ids are scalar loads
+// fetched one tile ahead of the tile loads.  A workgroup is one wave; the
+// launch order keeps all row groups of one (sequence, KV head) on one XCD
+// (workgroup i runs on XCD i % 8), latest positions first, so the re-reads
+// of a tile by other row groups hit that XCD's L2.
 //
 // fp32 kernel.  One wave per (query row, head): lanes hold D / 64 dims each;
 // each token's dot product is reduced across the wave.  It exists for the
