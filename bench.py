@@ -406,29 +406,55 @@ def prefill_flops(w):
     return f * w.num_heads * 4 * w.head_dim
 
 
-def prefill_cpu_baseline(w, budget_s=12.0):
-    """The oracle's prefill (fp64 NumPy, as it is) on (sequence, KV head)
-    units of the same workload until ~budget_s, scaled to TFLOP/s."""
+def _cpu_prefill_units(units):
+    """Worker: the oracle's prefill of (sequence, KV head) units; returns the
+    flops they hold."""
     import oracle
-
-    r = oracle.run_prefill(w, seqs=[], kv_heads=[])
-    qb = oracle.to_bits(w.q, w.dtype)
+    st = _CPU
+    w = st["w"]
     G = w.num_heads // w.num_kv_heads
-    units, flops = 0, 0
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
-        s, g = units % w.num_seqs, (units // w.num_seqs) % w.num_kv_heads
-        oracle.prefill(qb, r["k_pool"], r["v_pool"], w.block_tables, w.context_lens,
+    flops = 0
+    for s, g in units:
+        oracle.prefill(st["q"], st["k"], st["v"], w.block_tables, w.context_lens,
                        w.query_start, w.scale, w.num_kv_heads, w.block_size, w.dtype,
                        seqs=[s], kv_heads=[g])
         L, n = int(w.context_lens[s]), int(w.query_lens[s])
         flops += sum(max(L - n + i + 1, 0) for i in range(n)) * G * 4 * w.head_dim
-        units += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{units} (sequence, KV head) units of the same workload, single thread, "
-                      f"{dt:.1f} s"}
+    return flops
+
+
+def prefill_cpu_baseline(w, cpu_seconds=48.0):
+    """The oracle's prefill (fp64 NumPy, as it is) on this host's cores: the
+    workload's (sequence, KV head) units dealt to a pool of worker processes
+    with one BLAS thread each, one unit per worker per round, for about
+    ``cpu_seconds`` of CPU time in all; scaled to TFLOP/s."""
+    import multiprocessing as mp
+
+    import oracle
+    n = cpu_workers()
+    r = oracle.run_prefill(w, seqs=[], kv_heads=[])
+    _CPU.clear()
+    _CPU.update(w=w, q=oracle.to_bits(w.q, w.dtype), k=r["k_pool"], v=r["v_pool"])
+    del r
+    units = [(s, g) for s in range(w.num_seqs) for g in range(w.num_kv_heads)]
+    budget = max(cpu_seconds / n, 1.0)
+    ctx = mp.get_context("fork")
+    done, flops = 0, 0
+    with ctx.Pool(n, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_worker_init_probe, range(n))  # every worker started before timing
+        t0 = time.perf_counter()
+        while True:
+            batch = [[units[(done + i) % len(units)]] for i in range(n)]
+            flops += sum(pool.map(_cpu_prefill_units, batch))
+            done += n
+            dt = time.perf_counter() - t0
+            if dt >= budget:
+                break
+    _CPU.clear()
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": n,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done} (sequence, KV head) units of the same workload over {n} worker "
+                      f"processes (one BLAS thread each), {dt:.1f} s"}
 
 
 def run_prefill_bench(args):
