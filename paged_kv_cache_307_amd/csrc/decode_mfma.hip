@@ -50,6 +50,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "schedule.h"
@@ -75,6 +76,7 @@ template <int D>
 struct Tile {
   uint4 k[D / 32];
   uint2 v[D / 16];
+  uint2 v2[D / 16];  // B = 32, a block's first tile: the second tile's V (see load_tile_b32)
   bool bad;  // a block id outside [0, num_blocks): the tile's results become NaN
 };
 
@@ -196,6 +198,66 @@ __device__ __forceinline__ void load_tile(Tile<D>& r, const DecodeArgs& a, const
   }
 }
 
+// B = 32 in plain runs: the two 16-token tiles of a block whose tokens span
+// both halves (32 blk + 16 < L) take the tokens {0-3, 8-11, 16-19, 24-27}
+// and {4-7, 12-15, 20-23, 28-31} of the block, in that order (a matrix
+// product sums over its k index in any order, as long as P^T and V^T agree;
+// the masks and the appended row follow the same numbering).  Row r of the
+// first tile is block token 8 (r / 4) + r % 4, of the second that + 4, so
+// lane group g's V tokens of both tiles, 8g .. 8g + 7, are one 16-byte piece
+// of each dim row: the first tile's load fetches whole 64-byte dim rows
+// (whole 128-byte lines), keeping the second tile's half in v2, and the
+// second tile loads only its K rows.  A last block of at most 16 tokens is
+// one tile in plain order.  What a load site fetches of V is fixed at
+// compile time (the run's parity fixes which tiles come where), so each
+// wait covers exactly the loads it needs.
+enum VLoad { kVWide = 0, kVHalf = 1, kVNone = 2 };
+
+template <int D, int kV, bool kStream>
+__device__ __forceinline__ void load_tile_b32(Tile<D>& r, const DecodeArgs& a, const TileIds& id,
+                                              int kvh, int t0, int L, int lane, uint32_t k_off,
+                                              uint32_t k_off_pair) {
+  constexpr int B = 32;
+  constexpr int kTileBytes = B * D * 2;
+  constexpr int kPol = kStream ? kStreamOnce : 0;
+  const int col = lane & 15, grp = lane >> 4;
+  const bool bad = unsigned(id.pb0) >= unsigned(a.num_blocks);
+  const int pb = bad ? 0 : id.pb0;
+  const int64_t tile = (int64_t(pb) * a.num_kv_heads + kvh) * kTileBytes;
+  const int blk0 = t0 & ~(B - 1);
+  const int half = (t0 / kTile) & 1;
+  const bool paired = blk0 + kTile < L;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+  const __amdgpu_buffer_rsrc_t rk =
+      tile_rsrc(kc + tile + (paired ? half * 4 * D * 2 : half * kTile * D * 2), kTileBytes);
+  const uint32_t ko = paired ? k_off_pair : k_off;
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    r.k[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 64 * j, kPol));
+  if constexpr (kV != kVNone) {
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + tile, kTileBytes);
+    const uint32_t vrow = uint32_t(col) * B * 2;
+    if constexpr (kV == kVWide) {
+      // paired: tokens 8g .. 8g + 7; a one-tile block: tokens 4g .. 4g + 3 (low half)
+      const uint32_t vo = vrow + uint32_t(grp) * (paired ? 16 : 8);
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        const u32x4_t t = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, vo, 32 * B * c, kPol));
+        r.v[c] = make_uint2(t.x, t.y);
+        r.v2[c] = make_uint2(t.z, t.w);
+      }
+    } else {  // a block's second tile on its own (its run starts there)
+      const uint32_t vo = vrow + uint32_t(grp) * 16 + 8;
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        r.v[c] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vo, 32 * B * c, kPol));
+    }
+  }
+  r.bad = bad;
+}
+
 // IEEE maximum (a NaN operand gives NaN): one v_maximum3_f32, where fmaxf
 // first quiets every operand not known to be canonical (lane swap results,
 // matrix-core outputs) with an extra v_max_f32.  Only tile maxima use it; a
@@ -298,7 +360,8 @@ __device__ __forceinline__ void put_new_row(Tile<D>& r, const uint32_t* lds, int
 template <int D, int B>
 __device__ __forceinline__ void store_tile_back(const Tile<D>& r, const DecodeArgs& a, int pb,
                                                 int kvh, int t0, int rt, int lane,
-                                                uint32_t k_off, uint32_t v_off) {
+                                                uint32_t k_off, uint32_t v_off,
+                                                bool paired = false) {
   constexpr int kTileBytes = B * D * 2;
   // the pools are writable when a row is appended (the API takes them non-const)
   char* kc = static_cast<char*>(const_cast<void*>(a.k_cache));
@@ -308,8 +371,17 @@ __device__ __forceinline__ void store_tile_back(const Tile<D>& r, const DecodeAr
   const int grp = lane >> 4;
   bool v_here = true;
   int64_t k_shift = 0, v_shift = 0;
-  if constexpr (B >= kTile) {
-    const int in_block = t0 % B;  // 0, or 16 when B == 32
+  if constexpr (B == 32) {
+    const int half = (t0 / kTile) & 1;
+    if (paired) {  // the numbering of load_tile_b32: row rt is block token 8 (rt / 4) + rt % 4 + 4 half
+      k_shift = (int64_t(8 * (rt / 4) + rt % 4 + 4 * half) - rt) * D * 2;  // from row rt (k_off)
+      v_shift = int64_t(grp) * 8 + half * 8;                              // 16 g + 8 half from 8 g (v_off)
+    } else {
+      k_shift = half * kTile * D * 2;
+      v_shift = half * kTile * 2;
+    }
+  } else if constexpr (B >= kTile) {
+    const int in_block = t0 % B;  // 0
     k_shift = in_block * D * 2;
     v_shift = in_block * 2;
   } else {  // the tile's second block holds tokens B .. 15
@@ -590,15 +662,20 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     staged = 0;
   };
 
-  // Per-lane byte offsets inside a tile.
+  // Per-lane byte offsets inside a tile (k_off_pair: K row col of a paired
+  // B = 32 tile, see load_tile_b32).
   const uint32_t k_off = uint32_t(col) * D * 2 + uint32_t(grp) * 16;
   const uint32_t v_off = uint32_t(col) * B * 2 + uint32_t(grp) * 8;
+  const uint32_t k_off_pair = uint32_t(8 * (col / 4) + col % 4) * D * 2 + uint32_t(grp) * 16;
+  // B = 32 plain runs use the paired numbering of load_tile_b32; grouped
+  // launches (whose tail runs may start inside a block's first tile) do not.
+  constexpr bool kPair = B == 32 && !kGroups;
 
   // Keeps an appending tile's write-back for later (see tb_lds), or stores
   // it now when both slots are taken.
-  auto write_back = [&](const Tile<D>& r, int pb, int kvh, int t0, int rt) {
+  auto write_back = [&](const Tile<D>& r, int pb, int kvh, int t0, int rt, bool paired) {
     if (tb_used == kTbSlots) {
-      store_tile_back<D, B>(r, a, pb, kvh, t0, rt, lane, k_off, v_off);
+      store_tile_back<D, B>(r, a, pb, kvh, t0, rt, lane, k_off, v_off, paired);
       return;
     }
     uint32_t* slot = tb_lds + tb_used * kTbDwords;
@@ -614,7 +691,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       tb_info[tb_used * 4 + 0] = pb;
       tb_info[tb_used * 4 + 1] = kvh;
       tb_info[tb_used * 4 + 2] = t0;
-      tb_info[tb_used * 4 + 3] = rt;
+      tb_info[tb_used * 4 + 3] = rt | (paired ? 0x100 : 0);
     }
     ++tb_used;
   };
@@ -626,7 +703,8 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       const int pb = wave_uniform(tb_info[i * 4 + 0]);
       const int kvh = wave_uniform(tb_info[i * 4 + 1]);
       const int t0 = wave_uniform(tb_info[i * 4 + 2]);
-      const int rt = wave_uniform(tb_info[i * 4 + 3]);
+      const int rtp = wave_uniform(tb_info[i * 4 + 3]);
+      const int rt = rtp & 0xFF;
       Tile<D> r;
 #pragma unroll
       for (int c = 0; c < DCH; ++c)
@@ -635,7 +713,7 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       for (int j = 0; j < KSTEPS; ++j)
         r.k[j] = *reinterpret_cast<const uint4*>(slot + D * 8 + (j * 4 + grp) * 4);
       r.bad = false;
-      store_tile_back<D, B>(r, a, pb, kvh, t0, rt, lane, k_off, v_off);
+      store_tile_back<D, B>(r, a, pb, kvh, t0, rt, lane, k_off, v_off, (rtp & 0x100) != 0);
     }
     tb_used = 0;
   };
@@ -667,7 +745,22 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     // Appending decode: the run holding the pair's last tile uses the step's
     // row (token L - 1) in that tile and writes the tile back with the row
     // in its slot.
-    const bool append = a.new_k != nullptr && tin + ntile == (L - tok0 + kTile - 1) / kTile;
+    // The tile holding token L - 1 (counted from tok0) and its row there:
+    // the last tile, or with the paired B = 32 numbering whichever half of
+    // the last block holds it.
+    int tile_new = (L - tok0 + kTile - 1) / kTile - 1;
+    int rt_new = L - 1 - tok0 - tile_new * kTile;
+    bool paired_new = false;
+    if constexpr (kPair) {
+      const int blk0 = (L - 1) & ~(B - 1);
+      const int off = L - 1 - blk0;
+      if (blk0 + kTile < L) {
+        paired_new = true;
+        tile_new = blk0 / kTile + ((off >> 2) & 1);
+        rt_new = 4 * (off >> 3) + (off & 3);
+      }
+    }
+    const bool append = a.new_k != nullptr && tile_new >= tin && tile_new < tin + ntile;
     NewRow<D> nr{};
     int pb_new = 0;
     if (append) {  // issued first: its wait below overlaps the table window's
@@ -746,7 +839,18 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     auto t0_of = [&](int k) { return t_begin + k * kTile; };
 
     auto consume = [&](Tile<D>& r, int k) {
-      const int valid = t_end - t0_of(k);  // >= 1
+      // this lane's first token (of 4) in the tile, and the end of the tokens
+      // the tile may hold: tokens from `limit` on are dropped
+      const int t0 = t0_of(k);
+      int first = t0 + 4 * grp, span_end = t0 + kTile, limit = t_end;
+      if constexpr (kPair) {
+        const int blk0 = t0 & ~(B - 1);
+        if (blk0 + kTile < L) {
+          first = blk0 + 8 * grp + 4 * ((t0 / kTile) & 1);
+          span_end = blk0 + B;
+        }
+        limit = L;
+      }
       floatx4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KSTEPS; ++j)
@@ -755,11 +859,10 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = sacc[i] * a.scale_log2e;
-      if (valid < kTile) {  // last, partial tile: drop tokens >= t_end
-        const int first = 4 * grp;
+      if (span_end > limit) {  // last, partial tile: drop tokens >= limit
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = (first + i < valid) ? x[i] : -INFINITY;
-        const int n = min(max(valid - first, 0), 4);
+        for (int i = 0; i < 4; ++i) x[i] = (first + i < limit) ? x[i] : -INFINITY;
+        const int n = min(max(limit - first, 0), 4);
         const uint32_t mx = (n >= 1 ? 0x0000FFFFu : 0u) | (n >= 2 ? 0xFFFF0000u : 0u);
         const uint32_t my = (n >= 3 ? 0x0000FFFFu : 0u) | (n >= 4 ? 0xFFFF0000u : 0u);
 #pragma unroll
@@ -802,40 +905,65 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
     // the next run of tiles is loaded when the current run starts.
     {
       constexpr int kWin = window_tiles<B>();
+      static_assert(!kPair || (kRing == 2 && kWin % 2 == 0), "paired tiles assume a 2-tile ring");
       Tile<D> ring[kRing];
+      uint2 carry[DCH];  // paired B = 32: a block's second tile's V, from its first tile
       int win = load_window(row, t_begin / B, nblk, lane);
       if (append) {
-        // the row goes to LDS for the last tile, which also writes it to its
-        // slot in the cache (only this wave reads that slot in this launch)
+        // the row goes to LDS for the tile holding it, which also writes it
+        // to its slot in the cache (only this wave reads that slot in this launch)
         stage_new_row<D>(nr, new_row_lds, lane);
       }
-      for (int k0 = 0; k0 < ntile; k0 += kWin) {
-        const int k1 = min(ntile, k0 + kWin);
-        const int wb = t0_of(k0) / B;
-        const int last = k1 - 1;
-        TileIds id;
+      // One tile's loads into a ring slot; kv: what of V the site fetches
+      // (paired B = 32 only: fixed per site by the run's parity).
+      auto load_at = [&](Tile<D>& r, const TileIds& id, int kd, auto kv) {
+        if constexpr (kPair)
+          load_tile_b32<D, decltype(kv)::value, kStream>(r, a, id, kvh, t0_of(kd), L, lane, k_off,
+                                                         k_off_pair);
+        else
+          load_tile<D, B, kStream>(r, a, id, kvh, t0_of(kd), lane, k_off, v_off);
+      };
+      // par: the run starts at a block's second tile (paired B = 32; 0 otherwise)
+      auto walk = [&](auto par) {
+        constexpr int P = decltype(par)::value;
+        for (int k0 = 0; k0 < ntile; k0 += kWin) {
+          const int k1 = min(ntile, k0 + kWin);
+          const int wb = t0_of(k0) / B;
+          const int last = k1 - 1;
+          TileIds id;
 #pragma unroll
-        for (int d = 0; d < kRing - 1; ++d) {
-          const int kd = min(k0 + d, last);
-          id = window_ids<B>(win, wb, t0_of(kd), nblk);
-          load_tile<D, B, kStream>(ring[d], a, id, kvh, t0_of(kd), lane, k_off, v_off);
-        }
-        id = window_ids<B>(win, wb, t0_of(min(k0 + kRing - 1, last)), nblk);
-        int nxt = win;  // issued after this window's first reads, so they do not wait for it
-        if (k1 < ntile) nxt = load_window(row, t0_of(k1) / B, nblk, lane);
-        for (int k = k0; k < k1; k += kRing) {
-#pragma unroll
-          for (int d = 0; d < kRing; ++d) {
+          for (int d = 0; d < kRing - 1; ++d) {
+            const int kd = min(k0 + d, last);
+            id = window_ids<B>(win, wb, t0_of(kd), nblk);
+            load_at(ring[d], id, kd, std::integral_constant<int, P == 0 ? kVWide : kVHalf>{});
+          }
+          id = window_ids<B>(win, wb, t0_of(min(k0 + kRing - 1, last)), nblk);
+          int nxt = win;  // issued after this window's first reads, so they do not wait for it
+          if (k1 < ntile) nxt = load_window(row, t0_of(k1) / B, nblk, lane);
+          // step d of the ring at tile k (k even): d is a compile-time index
+          auto step = [&](int k, auto dd) {
+            constexpr int d = decltype(dd)::value;
             const int kl = min(k + d + kRing - 1, last);
-            load_tile<D, B, kStream>(ring[(d + kRing - 1) % kRing], a, id, kvh, t0_of(kl), lane,
-                                     k_off, v_off);
+            // tile k + d + 1 is a block's first tile when P + d + 1 is even
+            load_at(ring[(d + kRing - 1) % kRing], id, kl,
+                    std::integral_constant<int, ((P + d + 1) & 1) == 0 ? kVWide : kVNone>{});
             id = window_ids<B>(win, wb, t0_of(min(k + d + kRing, last)), nblk);
             if (k + d < k1) {
-              if (append && k + d == ntile - 1) {
-                const int rt = t_end - 1 - t0_of(k + d);
-                put_new_row<D>(ring[d], new_row_lds, rt, col, grp);
+              if constexpr (kPair) {
+                if constexpr (((P + d) & 1) == 1) {  // a block's second tile
+                  if (d > 0 || k > k0) {              // its first tile came just before
+#pragma unroll
+                    for (int c = 0; c < DCH; ++c) ring[d].v[c] = carry[c];
+                  }
+                } else {
+#pragma unroll
+                  for (int c = 0; c < DCH; ++c) carry[c] = ring[d].v2[c];
+                }
+              }
+              if (append && k + d == tile_new - tin) {
+                put_new_row<D>(ring[d], new_row_lds, rt_new, col, grp);
                 if (unsigned(pb_new) < unsigned(a.num_blocks))
-                  write_back(ring[d], pb_new, kvh, t0_of(k + d), rt);
+                  write_back(ring[d], pb_new, kvh, t0_of(k + d), rt_new, paired_new);
               }
               consume(ring[d], k + d);
               if (kParts && --part_left == 0 && k + d + 1 < ntile) {
@@ -848,9 +976,22 @@ void decode_bf16_mfma_kernel(DecodeArgs a) {
                 l_run = 0.f;
               }
             }
+          };
+          static_assert(kRing == 2, "the ring's steps are spelled out for two tiles");
+          for (int k = k0; k < k1; k += kRing) {
+            step(k, std::integral_constant<int, 0>{});
+            step(k, std::integral_constant<int, 1>{});
           }
+          win = nxt;
         }
-        win = nxt;
+      };
+      if constexpr (kPair) {
+        if ((t_begin / kTile) & 1)
+          walk(std::integral_constant<int, 1>{});
+        else
+          walk(std::integral_constant<int, 0>{});
+      } else {
+        walk(std::integral_constant<int, 0>{});
       }
     }
 

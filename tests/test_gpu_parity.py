@@ -70,6 +70,25 @@ SHAPES = [  # (Hq, Hkv, D, B, dtype)
 ]
 
 
+@pytest.mark.parametrize("shape", [(16, 2, 128), (8, 2, 64), (32, 2, 256)],
+                         ids=lambda s: "Hq%d_Hkv%d_D%d" % s)
+def test_b32_block_halves(shape):
+    """B = 32: a block whose tokens span both halves is decoded as two tiles
+    that each take every other group of four tokens (one 16-byte V load
+    fetches both tiles' values).  Every length 1..96 three times over, so
+    runs start at either half of a block, blocks end in either half, and
+    the appended row (token L - 1) lies in either tile; split, single pass,
+    two launches, rows appended or written first."""
+    Hq, Hkv, D = shape
+    lengths = list(range(1, 97)) * 3
+    w = W.custom(lengths, Hq, Hkv, D, 32, "bf16", seed=307_060 + Hq + D)
+    ref = oracle.run_step(w)
+    for P in (0, 32, 512):
+        _check_step(w, P, ref=ref)
+        _check_step(w, P, ref=ref, append=True)
+    _check_step(w, 64, ref=ref, two_phase=True, append=True)
+
+
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "Hq%d_Hkv%d_D%d_B%d_%s" % s)
 def test_ragged_lengths(shape):
     Hq, Hkv, D, B, dt = shape
