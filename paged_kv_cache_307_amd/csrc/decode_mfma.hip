@@ -130,10 +130,10 @@ constexpr int kRawBufferWord3 = 0x00020000;
 // this raises the rate of the decode's random 4 KiB tile reads from ~5.7 to
 // ~6.4 TB/s.  When blocks are shared between sequences the default policy
 // keeps them in the caches for their other readers.  With B = 32 a 16-token
-// V tile covers half of each 128-byte line and the next tile reads the other
-// half from the L2: streaming V there costs more than it saves, streaming K
-// alone measured slower than the default policy for both, and even 8 KiB
-// block reads (both halves at once) gain nothing from the nt bit.
+// V tile in token order covers half of each 128-byte line and the next tile
+// reads the other half from the L2, so such tiles (grouped launches) keep
+// the default policy; plain runs number a block's two tiles so that one
+// load fetches whole V lines (load_tile_b32), and stream them.
 constexpr int kStreamOnce = 2;
 
 template <int B, bool kStream>
