@@ -61,22 +61,22 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache_307_amd/csrc/schedule.h",
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
-MEASURED_TRAFFIC_SHA256 = "a52214b290edce72378fb32f255697593327931b832bae0471c39d6b306f217b"
+MEASURED_TRAFFIC_SHA256 = "a44e49a19000648189ca52adc5f749bdb8865a934bcbcddf4d2ed51e19dea2a8"
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False, False): {
-        "bytes": 554206757, "fetch_bytes": 549378693, "write_bytes": 4828064},
+        "bytes": 553883115, "fetch_bytes": 549055051, "write_bytes": 4828064},
     ("long_context", 512, True, False, False): {
-        "bytes": 2719684712, "fetch_bytes": 2696345049, "write_bytes": 23339663},
+        "bytes": 2719888932, "fetch_bytes": 2696549290, "write_bytes": 23339642},
     ("shared_prefix_steady", 4096, True, False, True): {
-        "bytes": 480513915, "fetch_bytes": 453780065, "write_bytes": 26733850},
+        "bytes": 480544664, "fetch_bytes": 453810817, "write_bytes": 26733847},
     ("shared_prefix_fork", 4096, True, False, True): {
-        "bytes": 210932490, "fetch_bytes": 177702101, "write_bytes": 33230389},
+        "bytes": 210514710, "fetch_bytes": 177284523, "write_bytes": 33230187},
     ("mixed_lengths_B8", 8192, True, False, False): {
-        "bytes": 1659308740, "fetch_bytes": 1645859366, "write_bytes": 13449374},
+        "bytes": 1659087063, "fetch_bytes": 1645637691, "write_bytes": 13449372},
     ("mixed_lengths_B16", 8192, True, False, False): {
-        "bytes": 1661506045, "fetch_bytes": 1643862382, "write_bytes": 17643663},
+        "bytes": 1660389337, "fetch_bytes": 1642745674, "write_bytes": 17643663},
     ("mixed_lengths_B32", 8192, True, False, False): {
-        "bytes": 1642828211, "fetch_bytes": 1625184166, "write_bytes": 17644045},
+        "bytes": 1675370157, "fetch_bytes": 1653302801, "write_bytes": 22067356},
 }
 # The same two passes over `bench.py --workload llama3_8b_prefill` for
 # pa_prefill (summary: profiles/prefill_llama3_8b_prefill_hbm_bytes.md).
