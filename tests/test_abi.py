@@ -264,3 +264,62 @@ def test_context_parallel_calls_reject_before_launch(lib):
     assert mk(FAKE, FAKE, 0, 8, 2, None) == OK
     assert mk(None, FAKE, 4, 8, 2, None) == INVALID
     assert mk(FAKE, FAKE, 4, 1 << 30, 4, None) == UNSUPPORTED
+
+
+def shared_prefix_call(lib, fn="pa_decode_shared_prefix", **kw):
+    args = dict(out=FAKE, q=FAKE, key=None, value=None, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE,
+                gs=FAKE, pl=FAKE, ng=2, S=4, Hq=32, Hkv=8, D=128, B=16, NB=100, MB=64,
+                maxlen=1024, scale=0.088, P=512, ws=FAKE, wsb=1 << 30, dtype=BF16, flags=0)
+    args.update(kw)
+    a = args
+    return getattr(lib, fn)(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"], a["bt"],
+                            a["cl"], a["gs"], a["pl"], a["ng"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                            a["B"], a["NB"], a["MB"], a["maxlen"], a["scale"], a["P"], a["ws"],
+                            a["wsb"], a["dtype"], a["flags"], None)
+
+
+@pytest.mark.parametrize("fn", ["pa_decode_shared_prefix", "pa_decode_shared_prefix_partials"])
+@pytest.mark.parametrize("kw,expect", [
+    (dict(key=FAKE), INVALID),                # only one of key / value
+    (dict(value=FAKE), INVALID),
+    (dict(P=0), INVALID),                     # grouped launches are split launches
+    (dict(P=-16), INVALID),
+    (dict(ng=-1), INVALID),
+    (dict(ng=513), UNSUPPORTED),              # beyond the LDS group table
+    (dict(gs=None), INVALID),
+    (dict(pl=None), INVALID),
+    (dict(Hq=30, Hkv=8), INVALID),
+    (dict(D=96), UNSUPPORTED),
+    (dict(P=24), INVALID),
+    (dict(ws=None, wsb=0), WORKSPACE),
+    (dict(wsb=1000), WORKSPACE),
+    (dict(flags=2), INVALID),
+    (dict(key=FAKE, value=FAKE, S=0), OK),    # nothing to do: no launch
+    (dict(S=0), OK),
+    (dict(S=0, ng=0, gs=None, pl=None), OK),
+])
+def test_shared_prefix_rejects_before_launch(lib, fn, kw, expect):
+    assert shared_prefix_call(lib, fn, **kw) == expect
+
+
+def test_shared_prefix_workspace_size_formula(lib):
+    """The plain workspace's layout with a meta block over groups + S units
+    (four int32 per unit), then the same tail records, then (groups x Hkv +
+    1024) wide slots of (64 / G, 32 / G at D = 256) member records."""
+    def expect(S, Hq, Hkv, D, L, P, ng):
+        G = Hq // Hkv
+        parts = max(1, -(-L // P))
+        rec = G * D + (2 * G + 1 + 3) // 4 * 4
+        U = S + ng
+        meta = ((U * 16 + 7) // 8 * 8 + 16 + 255) // 256 * 256
+        members = (64 if D <= 128 else 32) // G
+        return meta + (S * Hkv * (4 + parts) + 4096) * rec * 4 + (ng * Hkv + 1024) * members * rec * 4
+    for args in [(256, 32, 8, 128, 2560, 4096, 16), (40, 16, 4, 128, 700, 512, 6),
+                 (12, 32, 2, 256, 4096, 64, 3), (5, 8, 8, 64, 100, 16, 0)]:
+        assert pa.decode_shared_prefix_workspace_bytes(*args) == expect(*args), args
+    # at least the plain workspace of the same launch
+    assert pa.decode_shared_prefix_workspace_bytes(64, 32, 8, 128, 4096, 512, 4) > \
+        pa.decode_workspace_bytes(64, 32, 8, 128, 4096, 512)
+    assert pa.decode_shared_prefix_workspace_bytes(4, 32, 8, 128, 1024, 0, 2) == 0
+    assert pa.decode_shared_prefix_workspace_bytes(4, 32, 8, 128, 1024, 512, 513) == 0
+    assert pa.decode_shared_prefix_workspace_bytes(4, 32, 8, 128, 1024, 512, -1) == 0
