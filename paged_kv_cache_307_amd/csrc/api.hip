@@ -130,12 +130,18 @@ constexpr int kPrefixWt = 6;
 constexpr int kPrefixLead = 52;
 
 // Line weights of a plain split launch, in the same quarter tiles: a tile
-// 4, a run's start 12.
+// 4, a run's start 12.  At B = 32 a run's start and end cost about 1.2 us
+// more (per-worker timelines of the mixed-length batch: its first tile may be
+// a block's second half, whose V the run loads on its own, and a run that
+// ends on a block's first tile also fetches the second's V), and the fitted
+// start is 20: the balanced cut at 12 left the workers with many short runs
+// finishing last.
 constexpr int kPlainWt = 4;
 constexpr int kPlainLead = 12;
+constexpr int kPlainLeadB32 = 20;
 
-void set_line_weights(DecodeArgs& a, bool groups) {
-  a.tail_lead = groups ? kTailLead : kPlainLead;
+void set_line_weights(DecodeArgs& a, bool groups, int block_size) {
+  a.tail_lead = groups ? kTailLead : (block_size >= 32 ? kPlainLeadB32 : kPlainLead);
   a.tail_wt = groups ? kTailWt : kPlainWt;
   a.prefix_lead = kPrefixLead;
   a.prefix_wt = kPrefixWt;
@@ -144,7 +150,7 @@ void set_line_weights(DecodeArgs& a, bool groups) {
 // Longest context the split-schedule size check should assume: a pair's
 // positions are its tiles times the heaviest weight plus a lead.
 int64_t weighted_len(int64_t max_len, bool groups) {
-  if (!groups) return max_len * kPlainWt + 16 * int64_t(kPlainLead);
+  if (!groups) return max_len * kPlainWt + 16 * int64_t(kPlainLeadB32);
   const int wt = kPrefixWt > kTailWt ? kPrefixWt : kTailWt;
   const int lead = kTailLead > kPrefixLead ? kTailLead : kPrefixLead;
   return max_len * wt + 16 * int64_t(lead);
@@ -237,7 +243,7 @@ int plan_decode(DecodePlan* plan, void* out, const void* q, const void* k_cache,
       a.num_groups = num_groups;
       a.prefix_members = prefix_members_for(head_dim, group);
     }
-    set_line_weights(a, groups);
+    set_line_weights(a, groups, block_size);
     a.workers = workers;
     a.partition_size = partition_size;
     a.max_partitions = int32_t(parts);
@@ -348,7 +354,7 @@ int merge_call(void* out, const int32_t* context_lens, const int32_t* group_star
     a.num_groups = num_groups;
     a.prefix_members = prefix_members_for(head_dim, group);
   }
-  set_line_weights(a, groups);
+  set_line_weights(a, groups, block_size);
   a.workers = workers;
   a.split = 1;
   a.num_seqs = num_seqs;

@@ -118,7 +118,7 @@ def random_cases():
     return out
 
 
-@pytest.mark.parametrize("weights", [(0, 1), (12, 4), (3, 2)])
+@pytest.mark.parametrize("weights", [(0, 1), (12, 4), (20, 4), (3, 2)])
 @pytest.mark.parametrize("case", CASES + random_cases())
 def test_schedule_invariants(case, weights):
     lengths, hkv, partition, workers = case
