@@ -61,31 +61,31 @@ sys.path.insert(0, ROOT)
 KERNEL_SOURCES = ["paged_kv_cache_307_amd/csrc/decode_mfma.hip", "paged_kv_cache_307_amd/csrc/schedule.h",
                   "paged_kv_cache_307_amd/csrc/device_common.h", "paged_kv_cache_307_amd/csrc/internal.h",
                   "paged_kv_cache_307_amd/csrc/api.hip", "paged_kv_cache_307_amd/build.py"]
-MEASURED_TRAFFIC_SHA256 = "a44e49a19000648189ca52adc5f749bdb8865a934bcbcddf4d2ed51e19dea2a8"
+MEASURED_TRAFFIC_SHA256 = "ed5dc107157bb0ec170e860cad13cd3f9d2ea2076cf9b5054b91598699d0b7d0"
 MEASURED_TRAFFIC = {
     ("llama3_8b_decode", 4096, True, False, False): {
-        "bytes": 553883115, "fetch_bytes": 549055051, "write_bytes": 4828064},
+        "bytes": 553875718, "fetch_bytes": 549047654, "write_bytes": 4828064},
     ("long_context", 512, True, False, False): {
-        "bytes": 2719888932, "fetch_bytes": 2696549290, "write_bytes": 23339642},
+        "bytes": 2719792933, "fetch_bytes": 2696453283, "write_bytes": 23339650},
     ("shared_prefix_steady", 4096, True, False, True): {
-        "bytes": 480544664, "fetch_bytes": 453810817, "write_bytes": 26733847},
+        "bytes": 480424679, "fetch_bytes": 453690791, "write_bytes": 26733888},
     ("shared_prefix_fork", 4096, True, False, True): {
-        "bytes": 210514710, "fetch_bytes": 177284523, "write_bytes": 33230187},
+        "bytes": 210521474, "fetch_bytes": 177291217, "write_bytes": 33230257},
     ("mixed_lengths_B8", 8192, True, False, False): {
-        "bytes": 1659087063, "fetch_bytes": 1645637691, "write_bytes": 13449372},
+        "bytes": 1659140015, "fetch_bytes": 1645690641, "write_bytes": 13449374},
     ("mixed_lengths_B16", 8192, True, False, False): {
-        "bytes": 1660389337, "fetch_bytes": 1642745674, "write_bytes": 17643663},
+        "bytes": 1660488179, "fetch_bytes": 1642844503, "write_bytes": 17643676},
     ("mixed_lengths_B32", 8192, True, False, False): {
-        "bytes": 1675370157, "fetch_bytes": 1653302801, "write_bytes": 22067356},
+        "bytes": 1675116276, "fetch_bytes": 1653133340, "write_bytes": 21982936},
 }
 # The same two passes over `bench.py --workload llama3_8b_prefill` for
 # pa_prefill (summary: profiles/prefill_llama3_8b_prefill_hbm_bytes.md).
 PREFILL_SOURCES = ["paged_kv_cache_307_amd/csrc/prefill.hip", "paged_kv_cache_307_amd/csrc/device_common.h",
                    "paged_kv_cache_307_amd/csrc/internal.h", "paged_kv_cache_307_amd/csrc/api.hip",
                    "paged_kv_cache_307_amd/build.py"]
-PREFILL_TRAFFIC_SHA256 = "7659e35804cfd172d62ced01be6b8c956ab3a7b05084c3911ba67a3c1e0af165"
+PREFILL_TRAFFIC_SHA256 = "9987b1b7b3fefdf83f6fac768495e20876b555a3c553e3f242a456fa801a3396"
 PREFILL_TRAFFIC = {
-    "llama3_8b_prefill": {"bytes": 297493969, "fetch_bytes": 230361468, "write_bytes": 67132501},
+    "llama3_8b_prefill": {"bytes": 297510225, "fetch_bytes": 230376054, "write_bytes": 67134171},
 }
 
 
