@@ -140,17 +140,23 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
     return r;
   };
 
-  // Records 0 .. kPairSlots - 1 sit in slots indexed by the pair, so their
-  // loads go out together with the meta block's, before the pair's record
-  // count is known; most pairs have no others.
+  // Records 0 .. kPairSlots - 1 sit in slots indexed by the pair, so in a
+  // plain launch their loads go out together with the meta block's, before
+  // the pair's record count is known; most pairs have no others.  A grouped
+  // launch needs the meta block before its prefix records anyway, so there
+  // the pair slots are loaded with those, only as many as hold records
+  // (a member's tail often has one): the fork step's merge read 52 MB, about
+  // 15 MB of them stale slots.
   constexpr int KF = (kPairSlots + PG - 1) / PG;  // pair slots per lane
   const int64_t fixed0 = pair_fixed_slot(a, s, kvh);
   Loaded fr[KF];
+  if constexpr (!kGroups) {
 #pragma unroll
-  for (int u = 0; u < KF; ++u) fr[u] = load_record(fixed0 + min(pg + u * PG, kPairSlots - 1));
-  // keep them ahead of the length and meta loads below: the compiler would
-  // otherwise sink them past the empty-sequence exit, after its wait
-  asm volatile("" ::: "memory");
+    for (int u = 0; u < KF; ++u) fr[u] = load_record(fixed0 + min(pg + u * PG, kPairSlots - 1));
+    // keep them ahead of the length and meta loads below: the compiler would
+    // otherwise sink them past the empty-sequence exit, after its wait
+    asm volatile("" ::: "memory");
+  }
 
   PairRecords pr;
   UnitRecords ur;
@@ -169,6 +175,11 @@ __global__ __launch_bounds__(kThreads * NW) void merge_kernel(DecodeArgs a, int 
   }
   if (pr.whole) return;  // written whole by its worker
   if constexpr (kGroups) {
+    // the live pair slots (clamped loads of a slot past the count re-read
+    // the last live one, which the cache serves)
+    const int live_last = max(min(pr.count, kPairSlots) - 1, 0);
+#pragma unroll
+    for (int u = 0; u < KF; ++u) fr[u] = load_record(fixed0 + min(pg + u * PG, live_last));
     // the prefix pieces: one wide slot per worker that streamed part of the
     // group's shared tokens for this KV head, this member's record in it.
     // A member shorter than a piece's tokens has l = 0 there: skipped.
