@@ -8,12 +8,15 @@ import torch
 import oracle
 import paged_kv_cache_307_amd as pa
 
-# Max abs error allowed against the fp64 oracle.  bf16: the weight and output
-# roundings (2^-9 relative each on |v|, |o| <= ~4) stay under 0.016.  fp32:
-# each exponent's relative error is ~2^-24 (1 + |logit - m|); with at most 8
-# such terms per weight, a logit range under 6 at the 1/sqrt(D) scale and
-# |v| < 5 the worst case is 8 * 2^-24 * 7 * 5 = 1.7e-5.
-TOL = {"f32": 2e-5, "bf16": 2e-2}
+# Max abs error allowed against the fp64 oracle: the stated target, 1e-5 for
+# fp32 and 2e-2 for bf16 inputs with fp32 accumulation.  bf16: the weight and
+# output roundings (2^-9 relative each on |v|, |o| <= ~4) stay under 0.016.
+# fp32: each exponent's relative error is ~2^-24 (1 + |logit - m|); if every
+# one of at most 8 such terms per weight took its worst case with the same
+# sign (a logit range under 6 at the 1/sqrt(D) scale, |v| < 5) the output
+# could be off by 8 * 2^-24 * 7 * 5 = 1.7e-5, but they are independent
+# roundings: measured maxima are ~1e-6, an order below the bound used.
+TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
 def torch_dtype(w):
